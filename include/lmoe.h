@@ -1,0 +1,173 @@
+/*
+ * lmoe.h — C ABI of the Stable LatentMoE layer forward pass on AMD gfx950 (MI355X).
+ *
+ * Pages cited (site and section):
+ *   [vxz]   vxz.us, "苏神复盘 Kimi K3：896 个专家背后，藏着哪些关键技术取舍？", sections 01 and 02.
+ *   [tahou] tahou.com K3 architecture write-up, sections SiTU激活优化, 归一化策略调整, 负载均衡优化.
+ *   [slm]   lukebest.github.io "Stable Latent MoE", sections 路由机制, Quantile Balancing,
+ *           Latent-Space MoE, SiTU 激活, 训练基础设施.
+ *
+ * Conventions shared by every call:
+ *   - Every tensor pointer is caller-owned DEVICE memory (hipMalloc / PyTorch), row-major, and
+ *     16-byte aligned. The library never allocates or frees device memory; scratch space is the
+ *     caller's `workspace` (size from lmoe_workspace_bytes).
+ *   - Calls only enqueue kernels on `stream` (a hipStream_t; NULL = the null stream) and never
+ *     synchronise with the host. Ragged expert sizes stay on the device.
+ *   - Arguments are validated before anything is enqueued; on an error the call returns a status
+ *     and enqueues nothing, so outputs are untouched. A failed launch returns LMOE_ERR_HIP. Faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - Storage types: `act_dtype` selects float32 or bfloat16 (bit pattern in uint16) for
+ *     activations and layer weights. Router weights, bias, scores, thresholds, gamma and combine
+ *     weights are always float32. Accumulation is float32.
+ *   - Concurrent calls that share output or workspace buffers race; distinct buffers are safe.
+ */
+#ifndef LMOE_H
+#define LMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LMOE_OK = 0,
+  LMOE_ERR_INVALID_ARGUMENT = 1, /* NULL or misaligned pointer, inconsistent shape */
+  LMOE_ERR_UNSUPPORTED = 2,      /* valid but outside what the kernels handle (see each call) */
+  LMOE_ERR_WORKSPACE = 3,        /* workspace NULL or smaller than lmoe_workspace_bytes() */
+  LMOE_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} lmoe_status;
+
+typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1 } lmoe_dtype;
+
+/* Layer shape. T tokens; D = d_model; L = d_latent; E routed experts; top_k = k; inter = routed
+ * expert inner size I; n_shared = S; inter_shared = I_s; n_bins = NB; beta1 / beta2 = SiTU gate
+ * bound and up-branch soft cap ([tahou] SiTU激活优化: 4 and 25); rms_eps for RMSNorm. */
+typedef struct {
+  int32_t T, d_model, d_latent, n_experts, top_k, inter, n_shared, inter_shared, n_bins;
+  float beta1, beta2, rms_eps;
+  int32_t act_dtype; /* lmoe_dtype */
+} lmoe_shape;
+
+/* Shape limits common to the calls (LMOE_ERR_UNSUPPORTED otherwise): d_model, d_latent, inter and
+ * inter_shared are multiples of 64; 0 < top_k < n_experts <= 8192; top_k <= 64; n_bins in
+ * [2, 65536]; d_latent <= 8192; T >= 0 (T = 0 is a no-op). */
+
+enum { LMOE_CALL_ROUTE = 0, LMOE_CALL_PERMUTE = 1, LMOE_CALL_GROUPED_GLU = 2 };
+
+/* Bytes of workspace `which_call` needs for this shape (0 when none). For LMOE_CALL_GROUPED_GLU
+ * the value covers any group count up to max(n_experts, 1). */
+size_t lmoe_workspace_bytes(const lmoe_shape* shape, int which_call);
+
+/* Human-readable name of a status. */
+const char* lmoe_status_string(lmoe_status status);
+
+/* A1 + A2: router scores, biased top-k selection and combine weights.
+ * [slm] 路由机制 (router over x, then top-K); [vxz] 02 (per-expert selection bias, no aux loss).
+ *   x            [T, D] act_dtype         token activations
+ *   w_router     [E, D] f32               router weights
+ *   bias         [E] f32                  quantile-balancing selection bias b
+ *   logit_offset [E] f32 or NULL          added to the logits before the sigmoid
+ *   scores       [T, E] f32   (out)       s = sigmoid(x . w_router^T + logit_offset)
+ *   topk_idx     [T, k] i32   (out)       experts in rank order of s + b (descending; ties go to the
+ *                                         lower expert index)
+ *   topk_w       [T, k] f32   (out)       s of the selected experts divided by their sum
+ *   thresh       [T, 2] f32   (out)       k-th and (k+1)-th largest s + b of the row
+ *   workspace    LMOE_CALL_ROUTE bytes    (bf16 activations: a three-way bf16 split of w_router so
+ *                                         the products are exact and accumulate in f32)          */
+lmoe_status lmoe_route(const lmoe_shape* shape, const void* x, const float* w_router, const float* bias,
+                       const float* logit_offset, float* scores, int32_t* topk_idx, float* topk_w,
+                       float* thresh, void* workspace, size_t workspace_bytes, void* stream);
+
+/* A3: quantile-balancing histogram ([vxz] 02; [tahou] 负载均衡优化: bin the scores after mapping
+ * them to 0..1, and add histograms across micro-batches).
+ * For every (t, e): s_hat = scores + bias (f32 add); theta = thresh[t,1] if e is among the top-k of
+ * t, else thresh[t,0]; m = s_hat - theta; u = clamp((m + 1) * 0.5, 0, 1);
+ * bin = min(NB - 1, floor(u * NB)); hist[e, bin] += 1. Each step is one f32 operation.
+ *   scores [T,E] f32, bias [E] f32, topk_idx [T,k] i32, thresh [T,2] f32: as written by lmoe_route
+ *   hist   [E, NB] u32 (in/out)           incremented (never cleared here)                       */
+lmoe_status lmoe_qb_histogram(const lmoe_shape* shape, const float* scores, const float* bias,
+                              const int32_t* topk_idx, const float* thresh, uint32_t* hist, void* stream);
+
+/* A4: quantile-balancing bias update at a step boundary ([vxz] 02; [slm] Quantile Balancing).
+ * Per expert, in f64: c* = (E - k) * n_acc / E; j* = first bin with cumulative count >= c*;
+ * u_hat = (j* + (c* - cum(j* - 1)) / hist[e, j*]) / NB; m_hat = 2 u_hat - 1;
+ * bias[e] = (float)((double)bias[e] - m_hat). Then hist is zeroed. n_acc = tokens counted into
+ * hist since the last update; n_acc <= 0 leaves bias unchanged (hist is still zeroed).
+ *   hist [E, NB] u32 (in/out), bias [E] f32 (in/out)                                             */
+lmoe_status lmoe_qb_update(const lmoe_shape* shape, uint32_t* hist, int64_t n_acc, float* bias, void* stream);
+
+/* A5 + A6: down-projection to the latent space and permutation of (token, slot) pairs by expert
+ * ([vxz] 01: tokens are compressed to d_latent before being dispatched to the routed experts;
+ * [slm] 训练基础设施: static shapes, no host synchronisation).
+ *   x              [T, D] act_dtype
+ *   w_down         [L, D] act_dtype
+ *   topk_idx       [T, k] i32
+ *   x_lat          [T, L] act_dtype (out)   x . w_down^T
+ *   expert_offsets [E + 1] i32 (out)        first sorted row of each expert; [E] = T*k
+ *   sorted_token   [T*k] i32 (out)          token of each sorted row (tokens ascending per expert)
+ *   slot_of_pair   [T*k] i32 (out)          sorted row of pair t*k + j
+ *   x_perm         [T*k, L] act_dtype (out) x_lat[sorted_token[r]]
+ *   workspace      LMOE_CALL_PERMUTE bytes                                                         */
+lmoe_status lmoe_permute(const lmoe_shape* shape, const void* x, const void* w_down, const int32_t* topk_idx,
+                         void* x_lat, int32_t* expert_offsets, int32_t* sorted_token, int32_t* slot_of_pair,
+                         void* x_perm, void* workspace, size_t workspace_bytes, void* stream);
+
+/* A7 + A8 (and A10 with one group): grouped SiTU-GLU FFN over ragged row groups.
+ * [tahou] SiTU激活优化 and [slm] SiTU 激活: gate = first half of the first projection, up = second
+ * half; h = beta1*tanh(g/beta1)*sigmoid(g) * beta2*tanh(u/beta2) in f32, fused in the epilogue.
+ * For group g with rows [off[g], off[g+1]):
+ *   [g | u] = a[rows] . w1[g]^T ;  h[rows] = SiTU-GLU ;  y[rows] = h[rows] . w2[g]^T
+ *   n_groups      G >= 1
+ *   rows          total rows of a, h, y (= group_offsets[G])
+ *   K             input width (multiple of 64), inter: inner size (multiple of 64),
+ *   n_out         output width (multiple of 32)
+ *   a             [rows, K] act_dtype
+ *   group_offsets [G + 1] i32 device, non-decreasing, [0] = 0; NULL means one group of all rows
+ *   w1            [G, 2*inter, K] act_dtype (gate rows 0..inter-1, up rows inter..2*inter-1)
+ *   w2            [G, n_out, inter] act_dtype
+ *   h             [rows, inter] act_dtype (out)
+ *   y             [rows, n_out] y_dtype (out; y_dtype is LMOE_F32 or act_dtype)
+ *   workspace     LMOE_CALL_GROUPED_GLU bytes (device tile list)                                 */
+lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* shape, int32_t n_groups, int32_t rows, int32_t K,
+                                  int32_t inter, int32_t n_out, const void* a, const int32_t* group_offsets,
+                                  const void* w1, const void* w2, void* h, void* y, int32_t y_dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Shared experts as one FFN ([vxz] 01: always-on shared experts; by linearity S SiTU-GLU experts
+ * equal one of inner size S*I_s with the gate blocks, up blocks and down blocks concatenated).
+ * One-time weight repack, not part of the per-batch pass:
+ *   w1s [S, 2*I_s, D] -> w1s_packed [2*S*I_s, D] = gates of experts 0..S-1, then their up rows
+ *   w2s [S, D, I_s]   -> w2s_packed [D, S*I_s]   = [w2s[0] | w2s[1] | ...]                        */
+lmoe_status lmoe_pack_shared(const lmoe_shape* shape, const void* w1s, const void* w2s, void* w1s_packed,
+                             void* w2s_packed, void* stream);
+
+/* A9 + A11: router-weighted combine, RMSNorm, up-projection and shared-expert add
+ * ([vxz] 02 and [tahou] 归一化策略调整: the norm sits after the aggregation and before the
+ * up-projection; no extra scaling factor).
+ *   y_perm       [T*k, L] act_dtype       routed expert outputs in sorted-row order
+ *   slot_of_pair [T*k] i32
+ *   topk_w       [T, k] f32
+ *   gamma        [L] f32 or NULL (= ones)
+ *   w_up         [D, L] act_dtype
+ *   y_shared     [T, D] f32 or NULL       added before the final rounding
+ *   n_out        [T, L] act_dtype (out)   n = gamma * z / sqrt(mean(z^2) + eps), z = sum_j w_tj y(t,j)
+ *   out          [T, D] act_dtype (out)   n . w_up^T + y_shared                                    */
+lmoe_status lmoe_combine_norm_up(const lmoe_shape* shape, const void* y_perm, const int32_t* slot_of_pair,
+                                 const float* topk_w, const float* gamma, const void* w_up,
+                                 const float* y_shared, void* n_out, void* out, void* stream);
+
+/* Kernel timing for measurement. When enabled, every kernel the library enqueues is bracketed by
+ * HIP events on its stream. lmoe_profile_collect() synchronises those events and folds them into
+ * per-kernel totals; lmoe_profile_get() reads the totals of kernel `name` (count of launches and
+ * summed milliseconds). Host-side state, not thread-safe: a measurement aid only. */
+void lmoe_profile_enable(int on);
+void lmoe_profile_reset(void);
+lmoe_status lmoe_profile_collect(void);
+int lmoe_profile_get(const char* name, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LMOE_H */

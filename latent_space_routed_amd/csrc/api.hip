@@ -1,0 +1,297 @@
+// C ABI of the library: argument validation (before anything is enqueued), workspace sizing and the
+// composition of kernels behind each call.
+#include "common.h"
+
+using namespace lmoe;
+
+namespace {
+
+constexpr int kMaxExperts = 2048;  // top-k keeps 32 scores per lane; the permutation keeps 4 x E masks in LDS
+constexpr int kMaxTopK = 64;
+constexpr int kMaxBins = 32768;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int esize(int dtype) { return dtype == LMOE_BF16 ? 2 : 4; }
+
+lmoe_status check_shape(const lmoe_shape* sh) {
+  if (!sh) return LMOE_ERR_INVALID_ARGUMENT;
+  if (sh->act_dtype != LMOE_F32 && sh->act_dtype != LMOE_BF16) return LMOE_ERR_INVALID_ARGUMENT;
+  if (sh->T < 0 || sh->d_model <= 0 || sh->d_latent <= 0 || sh->n_experts <= 0 || sh->top_k <= 0 ||
+      sh->inter <= 0 || sh->n_shared < 0 || sh->inter_shared < 0 || sh->n_bins <= 0)
+    return LMOE_ERR_INVALID_ARGUMENT;
+  if (sh->top_k >= sh->n_experts) return LMOE_ERR_INVALID_ARGUMENT;  // the (k+1)-th score must exist
+  if (!(sh->beta1 > 0.0f) || !(sh->beta2 > 0.0f) || !(sh->rms_eps >= 0.0f)) return LMOE_ERR_INVALID_ARGUMENT;
+  if (sh->n_experts > kMaxExperts || sh->top_k > kMaxTopK || sh->n_bins < 2 || sh->n_bins > kMaxBins)
+    return LMOE_ERR_UNSUPPORTED;
+  if (sh->d_model % 64 || sh->d_latent % 64 || sh->inter % 64 || sh->inter_shared % 64) return LMOE_ERR_UNSUPPORTED;
+  if ((int64_t)sh->d_latent * esize(sh->act_dtype) / 16 > 1024) return LMOE_ERR_UNSUPPORTED;  // combine row in registers
+  if ((int64_t)sh->T * sh->top_k > 0x7fffffffLL) return LMOE_ERR_UNSUPPORTED;
+  return LMOE_OK;
+}
+
+lmoe_status hip_status(hipError_t e) { return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP; }
+
+GemmArgs gemm_args() {
+  GemmArgs a{};
+  a.beta1 = 4.0f;
+  a.beta2 = 25.0f;
+  a.G = 1;
+  return a;
+}
+
+// Tile shape: 256x256 blocks when they still give every CU work, else 128x128.
+GemmShape dense_shape(int64_t M, int64_t N_tile_cols_big) {
+  const int64_t tiles = ceil_div(M, 256) * N_tile_cols_big;
+  return tiles >= 256 ? GemmShape::Big : GemmShape::Small;
+}
+
+size_t route_ws(const lmoe_shape* sh) {
+  return sh->act_dtype == LMOE_BF16 ? round_up((size_t)3 * sh->n_experts * sh->d_model * 2) : 0;
+}
+size_t permute_ws(const lmoe_shape* sh) {
+  return round_up((size_t)ceil_div(sh->T > 0 ? sh->T : 1, kPermChunk) * sh->n_experts * 4);
+}
+size_t glu_ws(int groups) { return round_up((size_t)(groups + 1) * 4); }
+
+}  // namespace
+
+extern "C" {
+
+const char* lmoe_status_string(lmoe_status s) {
+  switch (s) {
+    case LMOE_OK: return "LMOE_OK";
+    case LMOE_ERR_INVALID_ARGUMENT: return "LMOE_ERR_INVALID_ARGUMENT";
+    case LMOE_ERR_UNSUPPORTED: return "LMOE_ERR_UNSUPPORTED";
+    case LMOE_ERR_WORKSPACE: return "LMOE_ERR_WORKSPACE";
+    case LMOE_ERR_HIP: return "LMOE_ERR_HIP";
+  }
+  return "LMOE_UNKNOWN_STATUS";
+}
+
+size_t lmoe_workspace_bytes(const lmoe_shape* sh, int which) {
+  if (check_shape(sh) != LMOE_OK) return 0;
+  switch (which) {
+    case LMOE_CALL_ROUTE: return route_ws(sh);
+    case LMOE_CALL_PERMUTE: return permute_ws(sh);
+    case LMOE_CALL_GROUPED_GLU: return glu_ws(sh->n_experts > 1 ? sh->n_experts : 1);
+  }
+  return 0;
+}
+
+lmoe_status lmoe_route(const lmoe_shape* sh, const void* x, const float* w_router, const float* bias,
+                       const float* logit_offset, float* scores, int32_t* topk_idx, float* topk_w, float* thresh,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  lmoe_status st = check_shape(sh);
+  if (st != LMOE_OK) return st;
+  if (sh->T == 0) return LMOE_OK;
+  if (!aligned16(x) || !aligned16(w_router) || !aligned4(bias) || !aligned16(scores) || !aligned4(topk_idx) ||
+      !aligned4(topk_w) || !aligned4(thresh) || (logit_offset && !aligned4(logit_offset)))
+    return LMOE_ERR_INVALID_ARGUMENT;
+  const size_t need = route_ws(sh);
+  if (need && (!workspace || workspace_bytes < need || !aligned16(workspace))) return LMOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = sh->T, D = sh->d_model, E = sh->n_experts;
+  GemmArgs a = gemm_args();
+  a.A = x;
+  a.lda = D;
+  a.a_kwrap = D;
+  a.C = scores;
+  a.ldc = E;
+  a.c_dtype = LMOE_F32;
+  a.M = T;
+  a.N = E;
+  a.col_bias = logit_offset;
+  a.tag = "gemm_router";
+  if (sh->act_dtype == LMOE_BF16) {
+    uint16_t* wsplit = static_cast<uint16_t*>(workspace);
+    st = hip_status(launch_split3(w_router, wsplit, E, D, s));
+    if (st != LMOE_OK) return st;
+    a.B = wsplit;
+    a.ldb = 3 * (int64_t)D;
+    a.K = 3 * D;
+  } else {
+    a.B = w_router;
+    a.ldb = D;
+    a.K = D;
+  }
+  st = hip_status(launch_gemm(a, sh->act_dtype, Epi::Sigmoid, dense_shape(T, ceil_div(E, 256)), s));
+  if (st != LMOE_OK) return st;
+  return hip_status(launch_topk(scores, bias, T, E, sh->top_k, topk_idx, topk_w, thresh, s));
+}
+
+lmoe_status lmoe_qb_histogram(const lmoe_shape* sh, const float* scores, const float* bias, const int32_t* topk_idx,
+                              const float* thresh, uint32_t* hist, void* stream) {
+  lmoe_status st = check_shape(sh);
+  if (st != LMOE_OK) return st;
+  if (sh->T == 0) return LMOE_OK;
+  if (!aligned4(scores) || !aligned4(bias) || !aligned4(topk_idx) || !aligned4(thresh) || !aligned4(hist))
+    return LMOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_qb_hist(scores, bias, topk_idx, thresh, sh->T, sh->n_experts, sh->top_k, sh->n_bins, hist,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+lmoe_status lmoe_qb_update(const lmoe_shape* sh, uint32_t* hist, int64_t n_acc, float* bias, void* stream) {
+  lmoe_status st = check_shape(sh);
+  if (st != LMOE_OK) return st;
+  if (!aligned4(hist) || !aligned4(bias)) return LMOE_ERR_INVALID_ARGUMENT;
+  if (n_acc > (int64_t(1) << 52) / (sh->n_experts > 0 ? sh->n_experts : 1)) return LMOE_ERR_UNSUPPORTED;
+  return hip_status(launch_qb_update(hist, sh->n_experts, sh->top_k, sh->n_bins, n_acc, bias,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+lmoe_status lmoe_permute(const lmoe_shape* sh, const void* x, const void* w_down, const int32_t* topk_idx,
+                         void* x_lat, int32_t* expert_offsets, int32_t* sorted_token, int32_t* slot_of_pair,
+                         void* x_perm, void* workspace, size_t workspace_bytes, void* stream) {
+  lmoe_status st = check_shape(sh);
+  if (st != LMOE_OK) return st;
+  if (sh->T == 0) {
+    // no tokens: every expert is empty (a fill kernel, not a memset node, so the call can be captured)
+    if (!aligned4(expert_offsets)) return LMOE_ERR_INVALID_ARGUMENT;
+    return hip_status(launch_fill_i32(expert_offsets, sh->n_experts + 1, 0, static_cast<hipStream_t>(stream)));
+  }
+  if (!aligned16(x) || !aligned16(w_down) || !aligned4(topk_idx) || !aligned16(x_lat) || !aligned4(expert_offsets) ||
+      !aligned4(sorted_token) || !aligned4(slot_of_pair) || !aligned16(x_perm))
+    return LMOE_ERR_INVALID_ARGUMENT;
+  const size_t need = permute_ws(sh);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return LMOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = sh->T, D = sh->d_model, L = sh->d_latent, E = sh->n_experts, k = sh->top_k;
+  GemmArgs a = gemm_args();
+  a.A = x;
+  a.lda = D;
+  a.a_kwrap = D;
+  a.B = w_down;
+  a.ldb = D;
+  a.C = x_lat;
+  a.ldc = L;
+  a.c_dtype = sh->act_dtype;
+  a.M = T;
+  a.N = L;
+  a.K = D;
+  a.tag = "gemm_down";
+  st = hip_status(launch_gemm(a, sh->act_dtype, Epi::Store, dense_shape(T, ceil_div(L, 256)), s));
+  if (st != LMOE_OK) return st;
+  st = hip_status(launch_permute(topk_idx, T, E, k, expert_offsets, sorted_token, slot_of_pair,
+                                 static_cast<int32_t*>(workspace), s));
+  if (st != LMOE_OK) return st;
+  return hip_status(launch_gather_rows(x_lat, slot_of_pair, T, k, (int64_t)L * esize(sh->act_dtype), x_perm, s));
+}
+
+lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* sh, int32_t G, int32_t rows, int32_t K, int32_t inter,
+                                  int32_t n_out, const void* a_in, const int32_t* group_offsets, const void* w1,
+                                  const void* w2, void* h, void* y, int32_t y_dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  lmoe_status st = check_shape(sh);
+  if (st != LMOE_OK) return st;
+  if (G < 1 || rows < 0 || K <= 0 || inter <= 0 || n_out <= 0) return LMOE_ERR_INVALID_ARGUMENT;
+  if (y_dtype != LMOE_F32 && y_dtype != sh->act_dtype) return LMOE_ERR_INVALID_ARGUMENT;
+  if (K % 64 || inter % 64) return LMOE_ERR_UNSUPPORTED;
+  if (!group_offsets && G != 1) return LMOE_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return LMOE_OK;
+  if (!aligned16(a_in) || !aligned16(w1) || !aligned16(w2) || !aligned16(h) || !aligned4(y) ||
+      (group_offsets && !aligned4(group_offsets)))
+    return LMOE_ERR_INVALID_ARGUMENT;
+  const size_t need = group_offsets ? glu_ws(G) : 0;
+  if (need && (!workspace || workspace_bytes < need || !aligned16(workspace))) return LMOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int dt = sh->act_dtype;
+
+  GemmShape shape;
+  if (group_offsets) {
+    shape = (int64_t)rows >= (int64_t)G * 64 ? GemmShape::Big : GemmShape::Small;
+    st = hip_status(launch_mtile_prefix(group_offsets, G, gemm_block_m(shape), static_cast<int32_t*>(workspace), s));
+    if (st != LMOE_OK) return st;
+  } else {
+    shape = dense_shape(rows, ceil_div(inter, 128));
+  }
+  const int32_t* mts = group_offsets ? static_cast<const int32_t*>(workspace) : nullptr;
+
+  GemmArgs g1 = gemm_args();
+  g1.A = a_in;
+  g1.lda = K;
+  g1.a_kwrap = K;
+  g1.B = w1;
+  g1.ldb = K;
+  g1.b_gstride = (int64_t)2 * inter * K;
+  g1.C = h;
+  g1.ldc = inter;
+  g1.c_dtype = dt;
+  g1.goff = group_offsets;
+  g1.mtile_start = mts;
+  g1.G = G;
+  g1.M = rows;
+  g1.N = inter;
+  g1.K = K;
+  g1.glu_up_off = inter;
+  g1.beta1 = sh->beta1;
+  g1.beta2 = sh->beta2;
+  g1.tag = group_offsets ? "gemm_glu_grouped" : "gemm_glu_dense";
+  st = hip_status(launch_gemm(g1, dt, Epi::Glu, shape, s));
+  if (st != LMOE_OK) return st;
+
+  GemmArgs g2 = g1;
+  g2.A = h;
+  g2.lda = inter;
+  g2.a_kwrap = inter;
+  g2.B = w2;
+  g2.ldb = inter;
+  g2.b_gstride = (int64_t)n_out * inter;
+  g2.C = y;
+  g2.ldc = n_out;
+  g2.c_dtype = y_dtype;
+  g2.N = n_out;
+  g2.K = inter;
+  g2.tag = group_offsets ? "gemm_down_grouped" : "gemm_out_dense";
+  if (!group_offsets) shape = dense_shape(rows, ceil_div(n_out, 256));
+  return hip_status(launch_gemm(g2, dt, Epi::Store, shape, s));
+}
+
+lmoe_status lmoe_pack_shared(const lmoe_shape* sh, const void* w1s, const void* w2s, void* w1s_packed,
+                             void* w2s_packed, void* stream) {
+  lmoe_status st = check_shape(sh);
+  if (st != LMOE_OK) return st;
+  if (sh->n_shared < 1 || sh->inter_shared < 64) return LMOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(w1s) || !aligned16(w2s) || !aligned16(w1s_packed) || !aligned16(w2s_packed))
+    return LMOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_pack_shared(w1s, w2s, sh->n_shared, sh->inter_shared, sh->d_model, esize(sh->act_dtype),
+                                       w1s_packed, w2s_packed, static_cast<hipStream_t>(stream)));
+}
+
+lmoe_status lmoe_combine_norm_up(const lmoe_shape* sh, const void* y_perm, const int32_t* slot_of_pair,
+                                 const float* topk_w, const float* gamma, const void* w_up, const float* y_shared,
+                                 void* n_out, void* out, void* stream) {
+  lmoe_status st = check_shape(sh);
+  if (st != LMOE_OK) return st;
+  if (sh->T == 0) return LMOE_OK;
+  if (!aligned16(y_perm) || !aligned4(slot_of_pair) || !aligned4(topk_w) || (gamma && !aligned4(gamma)) ||
+      !aligned16(w_up) || (y_shared && !aligned4(y_shared)) || !aligned16(n_out) || !aligned16(out))
+    return LMOE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = sh->T, D = sh->d_model, L = sh->d_latent;
+  st = hip_status(launch_combine_norm(y_perm, slot_of_pair, topk_w, gamma, T, sh->top_k, L, sh->rms_eps,
+                                      sh->act_dtype, n_out, s));
+  if (st != LMOE_OK) return st;
+  GemmArgs a = gemm_args();
+  a.A = n_out;
+  a.lda = L;
+  a.a_kwrap = L;
+  a.B = w_up;
+  a.ldb = L;
+  a.C = out;
+  a.ldc = D;
+  a.c_dtype = sh->act_dtype;
+  a.M = T;
+  a.N = D;
+  a.K = L;
+  a.residual = y_shared;
+  a.ldr = D;
+  a.tag = "gemm_up";
+  return hip_status(launch_gemm(a, sh->act_dtype, y_shared ? Epi::AddF32 : Epi::Store, dense_shape(T, ceil_div(D, 256)), s));
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// Router-weighted combine and RMSNorm, one wave per token ([vxz] 02; [tahou] 归一化策略调整: the
+// norm sits after the aggregation of the routed experts and before the up-projection).
+//   z = sum_j w[t, j] * y[slot(t, j)]   (f32, in rank order j = 0..k-1)
+//   n = gamma * z / sqrt(mean(z^2) + eps)
+// A lane owns CPL 16-byte chunks of the latent row (chunk c = lane + 64 i), so every y row is read
+// with fully coalesced 16-byte loads and z never leaves registers.
+#include "common.h"
+
+namespace lmoe {
+namespace {
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static inline void unpack(const uint4& v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static inline uint4 pack(const float* f) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(f[2 * i]) | ((uint32_t)f32_to_bf16(f[2 * i + 1]) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ static inline void unpack(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  __device__ static inline uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+};
+
+template <typename T, int CPL>
+__global__ void __launch_bounds__(256) combine_norm_kernel(const T* __restrict__ y, const int32_t* __restrict__ slot_of_pair,
+                                                           const float* __restrict__ w, const float* __restrict__ gamma,
+                                                           int T_, int k, int L, float eps, T* __restrict__ n_out) {
+  constexpr int V = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T_) return;
+  const int chunks = L / V;
+  float z[CPL][V];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i)
+#pragma unroll
+    for (int v = 0; v < V; ++v) z[i][v] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const int32_t slot = slot_of_pair[t * k + j];
+    if (slot < 0) continue;
+    const float wj = w[t * k + j];
+    const T* row = y + (int64_t)slot * L;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = lane + 64 * i;
+      if (c < chunks) {
+        float f[V];
+        Vec<T>::unpack(*reinterpret_cast<const uint4*>(row + (int64_t)c * V), f);
+#pragma unroll
+        for (int v = 0; v < V; ++v) z[i][v] += wj * f[v];
+      }
+    }
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i)
+#pragma unroll
+    for (int v = 0; v < V; ++v) ss += z[i][v] * z[i][v];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d);
+  const float r = 1.0f / sqrtf(ss / (float)L + eps);
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < chunks) {
+      float f[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) f[v] = (gamma ? gamma[c * V + v] : 1.0f) * (z[i][v] * r);
+      *reinterpret_cast<uint4*>(n_out + t * L + (int64_t)c * V) = Vec<T>::pack(f);
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_t(const void* y, const int32_t* sp, const float* w, const float* gamma, int T_, int k, int L,
+                    float eps, void* n, hipStream_t s) {
+  const int cpl = (int)ceil_div(L / Vec<T>::N, 64);
+  const dim3 grid((unsigned)ceil_div(T_, 4)), block(256);
+  const T* yy = static_cast<const T*>(y);
+  T* nn = static_cast<T*>(n);
+  if (cpl <= 1) hipLaunchKernelGGL((combine_norm_kernel<T, 1>), grid, block, 0, s, yy, sp, w, gamma, T_, k, L, eps, nn);
+  else if (cpl <= 2) hipLaunchKernelGGL((combine_norm_kernel<T, 2>), grid, block, 0, s, yy, sp, w, gamma, T_, k, L, eps, nn);
+  else if (cpl <= 4) hipLaunchKernelGGL((combine_norm_kernel<T, 4>), grid, block, 0, s, yy, sp, w, gamma, T_, k, L, eps, nn);
+  else if (cpl <= 8) hipLaunchKernelGGL((combine_norm_kernel<T, 8>), grid, block, 0, s, yy, sp, w, gamma, T_, k, L, eps, nn);
+  else if (cpl <= 16) hipLaunchKernelGGL((combine_norm_kernel<T, 16>), grid, block, 0, s, yy, sp, w, gamma, T_, k, L, eps, nn);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine_norm(const void* y, const int32_t* slot_of_pair, const float* w, const float* gamma, int T,
+                               int k, int L, float eps, int dtype, void* n_out, hipStream_t s) {
+  KernelTimer timer("combine_norm", s);
+  if (dtype == LMOE_BF16) return launch_t<uint16_t>(y, slot_of_pair, w, gamma, T, k, L, eps, n_out, s);
+  return launch_t<float>(y, slot_of_pair, w, gamma, T, k, L, eps, n_out, s);
+}
+
+}  // namespace lmoe

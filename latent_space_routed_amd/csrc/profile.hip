@@ -1,0 +1,90 @@
+// Optional per-kernel timing with HIP events recorded on the launch stream (a measurement aid).
+#include <map>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace lmoe {
+namespace {
+
+struct Pending {
+  const char* name;
+  hipEvent_t a, b;
+};
+struct Total {
+  int64_t launches = 0;
+  double ms = 0.0;
+};
+
+bool g_enabled = false;
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_pool;
+std::map<std::string, Total> g_totals;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+KernelTimer::KernelTimer(const char* n, hipStream_t s) : name(n), stream(s), ev0(nullptr) {
+  if (!g_enabled) return;
+  hipEvent_t e = take_event();
+  if (e && hipEventRecord(e, s) == hipSuccess) ev0 = e;
+}
+
+KernelTimer::~KernelTimer() {
+  if (!ev0) return;
+  hipEvent_t e = take_event();
+  if (e && hipEventRecord(e, stream) == hipSuccess) {
+    g_pending.push_back({name, static_cast<hipEvent_t>(ev0), e});
+  } else {
+    g_pool.push_back(static_cast<hipEvent_t>(ev0));
+    if (e) g_pool.push_back(e);
+  }
+}
+
+}  // namespace lmoe
+
+extern "C" {
+
+void lmoe_profile_enable(int on) { lmoe::g_enabled = on != 0; }
+
+void lmoe_profile_reset(void) { lmoe::g_totals.clear(); }
+
+lmoe_status lmoe_profile_collect(void) {
+  lmoe_status st = LMOE_OK;
+  for (auto& p : lmoe::g_pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess) {
+      st = LMOE_ERR_HIP;
+    } else {
+      auto& t = lmoe::g_totals[p.name];
+      t.launches += 1;
+      t.ms += ms;
+    }
+    lmoe::g_pool.push_back(p.a);
+    lmoe::g_pool.push_back(p.b);
+  }
+  lmoe::g_pending.clear();
+  return st;
+}
+
+int lmoe_profile_get(const char* name, int64_t* launches, double* total_ms) {
+  if (!name) return 0;
+  auto it = lmoe::g_totals.find(name);
+  if (it == lmoe::g_totals.end()) return 0;
+  if (launches) *launches = it->second.launches;
+  if (total_ms) *total_ms = it->second.ms;
+  return 1;
+}
+
+}  // extern "C"

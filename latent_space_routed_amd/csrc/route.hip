@@ -1,0 +1,250 @@
+// Routing and quantile balancing kernels: router-weight split, biased top-k, QB histogram, QB
+// bias update. All integer results (indices, bins, counts) are exact and order-independent.
+#include <math.h>
+
+#include "common.h"
+
+namespace lmoe {
+namespace {
+
+// ------------------------------------------------------------------------------------------------
+// Router weight split for exact products on bf16 MFMA: w = hi + mid + lo, each bf16, every
+// remainder exact in f32 (the error of rounding to a narrower format is representable in the
+// wider one). x (bf16) times a bf16 part has a 16-bit significand, so each product is exact in
+// f32 and the router logits accumulate in f32 like an f32 GEMM. Output row e = [hi | mid | lo].
+// ------------------------------------------------------------------------------------------------
+__global__ void split3_kernel(const float* __restrict__ w, uint16_t* __restrict__ out, int rows, int cols) {
+  const int64_t n = (int64_t)rows * cols;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / cols, c = i % cols;
+    const float v = w[i];
+    const uint16_t hi = f32_to_bf16(v);
+    const float r1 = v - bf16_to_f32(hi);
+    const uint16_t mid = f32_to_bf16(r1);
+    const float r2 = r1 - bf16_to_f32(mid);
+    const uint16_t lo = f32_to_bf16(r2);
+    uint16_t* o = out + r * 3 * cols + c;
+    o[0] = hi;
+    o[cols] = mid;
+    o[2 * (int64_t)cols] = lo;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Biased top-k, one wave per token row ([vxz] 02 selection bias; order: descending s + b, equal
+// values to the lower expert index). Lane l holds experts l, l+64, ... in registers; k+1 rounds of
+// (lane-local best, wave arg-max by shuffles) produce the ordered top-(k+1).
+// ------------------------------------------------------------------------------------------------
+__device__ inline bool better(float va, int ia, float vb, int ib) { return va > vb || (va == vb && ia < ib); }
+
+template <int NPL>
+__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ scores, const float* __restrict__ bias,
+                                                   int T, int E, int k, int32_t* __restrict__ idx,
+                                                   float* __restrict__ w, float* __restrict__ thresh) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = scores + t * E;
+  float v[NPL];
+  uint32_t taken = 0;  // bit i set: element i of this lane already selected or absent
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      v[i] = row[e] + bias[e];
+    } else {
+      v[i] = -INFINITY;
+      taken |= 1u << i;
+    }
+  }
+  int my_idx = -1;      // lane r keeps the r-th winner
+  float my_s = 0.0f;
+  float vk = 0.0f, vk1 = 0.0f;
+  for (int r = 0; r <= k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + 64 * i;
+      if (!(taken & (1u << i)) && better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const float ov = __shfl_xor(bv, d);
+      const int oi = __shfl_xor(bi, d);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane && bi < E) taken |= 1u << (bi >> 6);
+    if (r < k && lane == r) {
+      my_idx = bi;
+      my_s = row[bi];
+    }
+    if (r == k - 1) vk = bv;
+    if (r == k) vk1 = bv;
+  }
+  // sum of the selected unbiased scores: fixed-order tree over lanes 0..k-1
+  float sum = lane < k ? my_s : 0.0f;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
+  if (lane < k) {
+    idx[t * k + lane] = my_idx;
+    w[t * k + lane] = my_s / sum;
+  }
+  if (lane == 0) {
+    thresh[2 * t] = vk;
+    thresh[2 * t + 1] = vk1;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// QB histogram ([tahou] 负载均衡优化: map to 0..1 and bin). A workgroup owns a slice of EB experts
+// and a chunk of tokens; its [EB, NB] counters live in LDS and are flushed with one integer
+// atomic per non-zero bin. Selection of e by t is decided from the row's k-th value v_k and the
+// k-th expert index e_k (the order is value desc, index asc): e is selected iff
+// s_hat > v_k, or s_hat == v_k and e <= e_k.
+// ------------------------------------------------------------------------------------------------
+constexpr int kHistThreads = 512;
+constexpr int kHistLdsBytes = 128 * 1024;
+
+__global__ void __launch_bounds__(kHistThreads)
+    qb_hist_kernel(const float* __restrict__ scores, const float* __restrict__ bias, const int32_t* __restrict__ idx,
+                   const float* __restrict__ thresh, int T, int E, int k, int nb, int eb, int tchunk,
+                   uint32_t* __restrict__ hist) {
+  extern __shared__ uint32_t cnt[];  // [eb][nb]
+  const int e0 = blockIdx.x * eb;
+  const int t0 = blockIdx.y * tchunk;
+  const int t1 = min(T, t0 + tchunk);
+  for (int i = threadIdx.x; i < eb * nb; i += kHistThreads) cnt[i] = 0;
+  __syncthreads();
+  // threads cover (token lane, expert lane) = (tid / eb, tid % eb); eb divides 512
+  const int el = threadIdx.x % eb, tl = threadIdx.x / eb, tstep = kHistThreads / eb;
+  const int e = e0 + el;
+  if (e < E) {
+    const float be = bias[e];
+    const float fnb = (float)nb;
+    for (int t = t0 + tl; t < t1; t += tstep) {
+      const float vk = thresh[2 * (int64_t)t], vk1 = thresh[2 * (int64_t)t + 1];
+      const int ek = idx[(int64_t)t * k + k - 1];
+      const float sh = __fadd_rn(scores[(int64_t)t * E + e], be);
+      const bool sel = sh > vk || (sh == vk && e <= ek);
+      const float m = __fsub_rn(sh, sel ? vk1 : vk);
+      float u = __fmul_rn(__fadd_rn(m, 1.0f), 0.5f);
+      u = fminf(fmaxf(u, 0.0f), 1.0f);
+      const int b = min(nb - 1, (int)floorf(__fmul_rn(u, fnb)));
+      atomicAdd(&cnt[el * nb + b], 1u);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < eb * nb; i += kHistThreads) {
+    const uint32_t c = cnt[i];
+    const int ee = e0 + i / nb;
+    if (c != 0 && ee < E) atomicAdd(&hist[(int64_t)ee * nb + i % nb], c);
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// QB bias update, one wave per expert ([vxz] 02; [slm] Quantile Balancing). Lane l sums bins
+// [l*bpl, (l+1)*bpl); a wave scan gives each lane its cumulative base; the one lane whose range
+// crosses c* walks its bins to j*, interpolates in f64 and moves the bias; then the row is zeroed.
+// ------------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) qb_update_kernel(uint32_t* __restrict__ hist, int E, int k, int nb,
+                                                        int64_t n_acc, float* __restrict__ bias) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  uint32_t* h = hist + (int64_t)e * nb;
+  const int bpl = (nb + 63) / 64;
+  const int j0 = min(nb, lane * bpl), j1 = min(nb, j0 + bpl);
+  uint64_t lsum = 0;
+  for (int j = j0; j < j1; ++j) lsum += h[j];
+  uint64_t incl = lsum;  // inclusive wave scan
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  const uint64_t base = incl - lsum;
+  if (n_acc > 0) {
+    const double c_star = (double)((int64_t)(E - k) * n_acc) / (double)E;
+    if ((double)base < c_star && (double)incl >= c_star) {
+      uint64_t cum = base;
+      for (int j = j0; j < j1; ++j) {
+        const uint64_t hj = h[j];
+        if ((double)(cum + hj) >= c_star) {
+          const double frac = (c_star - (double)cum) / (double)hj;
+          const double u_hat = ((double)j + frac) / (double)nb;
+          const double m_hat = 2.0 * u_hat - 1.0;
+          bias[e] = (float)((double)bias[e] - m_hat);
+          break;
+        }
+        cum += hj;
+      }
+    }
+  }
+  for (int j = j0; j < j1; ++j) h[j] = 0;
+}
+
+template <int NPL>
+void launch_topk_t(const float* s, const float* b, int T, int E, int k, int32_t* idx, float* w, float* th,
+                   hipStream_t st) {
+  hipLaunchKernelGGL(topk_kernel<NPL>, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0, st, s, b, T, E, k, idx, w, th);
+}
+
+}  // namespace
+
+hipError_t launch_split3(const float* w, uint16_t* out, int rows, int cols, hipStream_t s) {
+  KernelTimer timer("router_split", s);
+  const int64_t n = (int64_t)rows * cols;
+  const unsigned blocks = (unsigned)hmin(ceil_div(n, 256), 8192);
+  hipLaunchKernelGGL(split3_kernel, dim3(blocks), dim3(256), 0, s, w, out, rows, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* idx, float* w,
+                       float* thresh, hipStream_t s) {
+  KernelTimer timer("route_topk", s);
+  const int npl = (int)ceil_div(E, 64);
+  if (npl <= 2) launch_topk_t<2>(scores, bias, T, E, k, idx, w, thresh, s);
+  else if (npl <= 4) launch_topk_t<4>(scores, bias, T, E, k, idx, w, thresh, s);
+  else if (npl <= 8) launch_topk_t<8>(scores, bias, T, E, k, idx, w, thresh, s);
+  else if (npl <= 16) launch_topk_t<16>(scores, bias, T, E, k, idx, w, thresh, s);
+  else if (npl <= 32) launch_topk_t<32>(scores, bias, T, E, k, idx, w, thresh, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_qb_hist(const float* scores, const float* bias, const int32_t* idx, const float* thresh, int T,
+                          int E, int k, int nb, uint32_t* hist, hipStream_t s) {
+  KernelTimer timer("qb_hist", s);
+  // experts per slice: a power of two dividing 512, with eb * nb counters fitting the LDS budget
+  int eb = 32;
+  while (eb > 1 && (int64_t)eb * nb * 4 > kHistLdsBytes) eb >>= 1;
+  if ((int64_t)eb * nb * 4 > kHistLdsBytes) return hipErrorInvalidValue;
+  const int slices = (int)ceil_div(E, eb);
+  const int want_chunks = (int)hmax(1, ceil_div(512, slices));
+  const int tchunk = (int)hmax(64, ceil_div(T, want_chunks));
+  const int chunks = (int)ceil_div(T, tchunk);
+  const size_t lds = (size_t)eb * nb * 4;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipFuncSetAttribute((const void*)qb_hist_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kHistLdsBytes);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(qb_hist_kernel, dim3(slices, chunks), dim3(kHistThreads), lds, s, scores, bias, idx, thresh, T,
+                     E, k, nb, eb, tchunk, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_qb_update(uint32_t* hist, int E, int k, int nb, int64_t n_acc, float* bias, hipStream_t s) {
+  KernelTimer timer("qb_update", s);
+  hipLaunchKernelGGL(qb_update_kernel, dim3((unsigned)ceil_div(E, 4)), dim3(256), 0, s, hist, E, k, nb, n_acc, bias);
+  return hipGetLastError();
+}
+
+}  // namespace lmoe

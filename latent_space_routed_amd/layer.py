@@ -1,0 +1,130 @@
+"""Stable LatentMoE layer forward composed from the C-ABI calls (device memory via PyTorch).
+
+Order of the calls ([vxz] 01-02 and [slm] Latent-Space MoE: route, dispatch in latent space, expert
+FFNs, combine, norm, up-project, shared experts added):
+  lmoe_route -> lmoe_qb_histogram -> lmoe_permute -> lmoe_grouped_situ_glu (routed experts)
+  -> lmoe_grouped_situ_glu (shared experts, one group) -> lmoe_combine_norm_up
+and, at a step boundary, lmoe_qb_update. Every step runs in the library's kernels; this module only
+allocates buffers and passes pointers.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as C
+
+_TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def to_device(a: np.ndarray | None, act_dtype: str, device="cuda") -> torch.Tensor | None:
+    """Host array -> device tensor. uint16 arrays are bfloat16 bit patterns."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+class LatentMoE:
+    """One layer instance: weights on the device, per-batch buffers sized for up to ``max_tokens``."""
+
+    def __init__(self, cfg, weights: dict, max_tokens: int | None = None, device: str = "cuda"):
+        self.cfg = cfg
+        self.device = device
+        self.max_tokens = cfg.T if max_tokens is None else max_tokens
+        self.w = weights
+        dt = _TORCH_DT[cfg.act_dtype]
+        self.dt = dt
+        E, NB, D, S, Is = cfg.n_experts, cfg.n_bins, cfg.d_model, cfg.n_shared, cfg.inter_shared
+        self.bias = weights["bias"].clone()
+        self.hist = torch.zeros(E, NB, dtype=torch.int32, device=device)
+        self.n_acc = 0
+        shape = C.make_shape(cfg, self.max_tokens)
+        self.w1s_packed = torch.empty(2 * S * Is, D, dtype=dt, device=device)
+        self.w2s_packed = torch.empty(D, S * Is, dtype=dt, device=device)
+        if S > 0:
+            C.lmoe_pack_shared(shape, weights["w1s"], weights["w2s"], self.w1s_packed, self.w2s_packed)
+        self._bufs = {}
+        self._alloc(self.max_tokens)
+
+    # -------------------------------------------------------------------------------------------
+    def _alloc(self, T: int) -> None:
+        cfg, dev, dt = self.cfg, self.device, self.dt
+        E, k, L, D, I = cfg.n_experts, cfg.top_k, cfg.d_latent, cfg.d_model, cfg.inter
+        S, Is = cfg.n_shared, cfg.inter_shared
+        shape = C.make_shape(cfg, T)
+        f32, i32 = torch.float32, torch.int32
+        b = {
+            "scores": torch.empty(T, E, dtype=f32, device=dev),
+            "idx": torch.empty(T, k, dtype=i32, device=dev),
+            "w": torch.empty(T, k, dtype=f32, device=dev),
+            "thresh": torch.empty(T, 2, dtype=f32, device=dev),
+            "x_lat": torch.empty(T, L, dtype=dt, device=dev),
+            "offsets": torch.empty(E + 1, dtype=i32, device=dev),
+            "sorted_token": torch.empty(T * k, dtype=i32, device=dev),
+            "slot_of_pair": torch.empty(T * k, dtype=i32, device=dev),
+            "x_perm": torch.empty(T * k, L, dtype=dt, device=dev),
+            "h": torch.empty(T * k, I, dtype=dt, device=dev),
+            "y": torch.empty(T * k, L, dtype=dt, device=dev),
+            "h_s": torch.empty(T, max(S * Is, 64), dtype=dt, device=dev),
+            "y_sh": torch.empty(T, D, dtype=f32, device=dev),
+            "n": torch.empty(T, L, dtype=dt, device=dev),
+            "out": torch.empty(T, D, dtype=dt, device=dev),
+        }
+        for name, which in (("ws_route", C.LMOE_CALL_ROUTE), ("ws_permute", C.LMOE_CALL_PERMUTE),
+                            ("ws_glu", C.LMOE_CALL_GROUPED_GLU)):
+            n = C.workspace_bytes(shape, which)
+            b[name] = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        self._bufs = b
+
+    # -------------------------------------------------------------------------------------------
+    def forward(self, x: torch.Tensor, accumulate_hist: bool = True) -> dict:
+        """One forward pass over x [T, D]; returns the buffers (views of the first T tokens)."""
+        cfg, w = self.cfg, self.w
+        T = x.shape[0]
+        if T > self.max_tokens:
+            self.max_tokens = T
+            self._alloc(T)
+        b = {k: (v[:T] if k in ("scores", "idx", "w", "thresh", "x_lat", "h_s", "y_sh", "n", "out") else v)
+             for k, v in self._bufs.items()}
+        for k in ("sorted_token", "slot_of_pair"):
+            b[k] = self._bufs[k][: T * cfg.top_k]
+        for k in ("x_perm", "h", "y"):
+            b[k] = self._bufs[k][: T * cfg.top_k]
+        shape = C.make_shape(cfg, T)
+        E, k, L, D, I = cfg.n_experts, cfg.top_k, cfg.d_latent, cfg.d_model, cfg.inter
+        S, Is = cfg.n_shared, cfg.inter_shared
+        C.lmoe_route(shape, x, w["w_router"], self.bias, w.get("logit_offset"), b["scores"], b["idx"], b["w"],
+                     b["thresh"], b["ws_route"])
+        if accumulate_hist:
+            C.lmoe_qb_histogram(shape, b["scores"], self.bias, b["idx"], b["thresh"], self.hist)
+            self.n_acc += T
+        C.lmoe_permute(shape, x, w["w_down"], b["idx"], b["x_lat"], b["offsets"], b["sorted_token"],
+                       b["slot_of_pair"], b["x_perm"], b["ws_permute"])
+        C.lmoe_grouped_situ_glu(shape, E, T * k, L, I, L, b["x_perm"], b["offsets"], w["w1"], w["w2"], b["h"],
+                                b["y"], b["ws_glu"])
+        y_sh = None
+        if S > 0:
+            C.lmoe_grouped_situ_glu(shape, 1, T, D, S * Is, D, x, None, self.w1s_packed, self.w2s_packed,
+                                    b["h_s"], b["y_sh"], b["ws_glu"])
+            y_sh = b["y_sh"]
+        C.lmoe_combine_norm_up(shape, b["y"], b["slot_of_pair"], b["w"], w.get("gamma"), w["w_up"], y_sh, b["n"],
+                               b["out"])
+        return b
+
+    def qb_update(self) -> None:
+        """Move the selection bias from the accumulated histogram and reset it (a step boundary)."""
+        C.lmoe_qb_update(C.make_shape(self.cfg, 0), self.hist, self.n_acc, self.bias)
+        self.n_acc = 0
+
+
+def upload_weights(inp: dict, act_dtype: str, device: str = "cuda") -> dict:
+    """The seeded host inputs (see workloads.inputs) as device tensors."""
+    out = {}
+    for name, a in inp.items():
+        if name == "x":
+            continue
+        out[name] = to_device(a, act_dtype, device)
+    return out
