@@ -1,0 +1,192 @@
+"""Benchmark: tokens/s of one Stable LatentMoE layer forward at K3 shape on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic tokens: route (router GEMM,
+top-k), QB histogram, down-projection + permutation, routed grouped SiTU-GLU FFNs, shared experts,
+combine + RMSNorm + up-projection, and the QB bias update. Inputs are resident in HBM before the
+timed region. Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload k3_prefill] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s per Stable LatentMoE layer fwd (K3 shape); % bf16 MFMA / HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+DOMINANT = "gemm_glu_grouped"  # routed experts' GEMM1 + SiTU-GLU epilogue
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_glu_grouped_k3_prefill.json")
+KERNEL_SOURCES = ("latent_space_routed_amd/csrc/gemm.hip", "latent_space_routed_amd/csrc/common.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def glu_bytes(cfg, offsets) -> tuple[float, float]:
+    """Algorithmic HBM bytes and FLOPs of one routed GEMM1 launch: the W1 slices of the experts that
+    received tokens, the permuted latent rows read once, and h written once."""
+    import numpy as np
+
+    counts = np.diff(offsets)
+    touched = int((counts > 0).sum())
+    rows = int(offsets[-1])
+    esz = 2 if cfg.act_dtype == "bf16" else 4
+    w_bytes = touched * 2 * cfg.inter * cfg.d_latent * esz
+    a_bytes = rows * cfg.d_latent * esz
+    h_bytes = rows * cfg.inter * esz
+    flops = 2.0 * rows * cfg.d_latent * 2 * cfg.inter
+    return float(w_bytes + a_bytes + h_bytes), flops
+
+
+def cpu_baseline(cfg, inp, sample_tokens: int) -> dict:
+    """The oracle as it stands, on a bounded sample of the same workload (host cores)."""
+    import numpy as np
+
+    from oracle import lmoe_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    sub = dict(inp)
+    sub["x"] = inp["x"][:sample_tokens]
+    cfg_s = cfg.with_tokens(sample_tokens)
+    t0 = time.perf_counter()
+    s, idx, w, thr = O.route(sub, cfg_s)
+    O.qb_histogram(s, sub["bias"], idx, thr, cfg.n_bins)
+    O.permute(idx, cfg.n_experts)
+    O.expert_path(sub, cfg_s, idx, w)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {sample_tokens} tokens of the {cfg.name} batch through the full forward "
+                      f"(route, QB histogram, permutation, all touched experts, shared, combine, norm, up): "
+                      f"{dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="k3_prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from latent_space_routed_amd import LatentMoE, _lib, to_device, upload_weights
+    from workloads import CONFIGS
+    from workloads.inputs import make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    cfg = CONFIGS[args.workload]
+    log(f"[bench] generating {cfg.name} inputs")
+    t0 = time.perf_counter()
+    inp = make_inputs(cfg)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+    w = upload_weights(inp, cfg.act_dtype)
+    x = to_device(inp["x"], cfg.act_dtype)
+    layer = LatentMoE(cfg, w)
+    torch.cuda.synchronize()
+
+    def step():
+        layer.forward(x)
+        layer.qb_update()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    _lib.profile_reset()
+    _lib.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    _lib.profile_enable(False)
+    _lib.profile_collect()
+    log(f"[bench] timed {args.steps} steps in {elapsed:.3f} s")
+
+    names = ["router_split", "gemm_router", "route_topk", "qb_hist", "gemm_down", "perm_count", "perm_scan",
+             "perm_scatter", "gather_rows", "mtile_prefix", "gemm_glu_grouped", "gemm_down_grouped",
+             "gemm_glu_dense", "gemm_out_dense", "combine_norm", "gemm_up", "qb_update"]
+    kernels = {}
+    for n in names:
+        cnt, ms = _lib.profile_get(n)
+        if cnt:
+            kernels[n] = round(ms / args.steps, 4)
+    cnt, ms = _lib.profile_get(DOMINANT)
+    avg_s = ms / cnt / 1e3
+    b = layer.forward(x)
+    torch.cuda.synchronize()
+    offsets = b["offsets"].cpu().numpy()
+    bytes_, flops = glu_bytes(cfg, offsets)
+    achieved = bytes_ / avg_s / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_digest") == source_digest() and tr.get("workload") == cfg.name:
+            traffic = tr.get("bytes_per_launch")
+
+    ms_per_step = elapsed / args.steps * 1e3
+    out = {
+        "metric": METRIC,
+        "value": cfg.T * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.act_dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d_model, "d_latent": cfg.d_latent,
+                   "n_experts": cfg.n_experts, "top_k": cfg.top_k, "inter": cfg.inter, "n_shared": cfg.n_shared,
+                   "inter_shared": cfg.inter_shared, "n_bins": cfg.n_bins, "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": DOMINANT, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes": bytes_, "avg_launch_ms": round(avg_s * 1e3, 4),
+                     "mfma_tflops": round(flops / avg_s / 1e12, 1),
+                     "mfma_frac": round(flops / avg_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "kernels_ms_per_step": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle on {args.cpu_sample} tokens")
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

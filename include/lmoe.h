@@ -50,9 +50,10 @@ typedef struct {
   int32_t act_dtype; /* lmoe_dtype */
 } lmoe_shape;
 
-/* Shape limits common to the calls (LMOE_ERR_UNSUPPORTED otherwise): d_model, d_latent, inter and
- * inter_shared are multiples of 64; 0 < top_k < n_experts <= 8192; top_k <= 64; n_bins in
- * [2, 65536]; d_latent <= 8192; T >= 0 (T = 0 is a no-op). */
+/* Shape limits common to the calls: 0 < top_k < n_experts and T >= 0 (T = 0 enqueues nothing but
+ * the zero offsets of lmoe_permute), else LMOE_ERR_INVALID_ARGUMENT; d_model, d_latent, inter and
+ * inter_shared multiples of 64, n_experts <= 2048, top_k <= 64, n_bins in [2, 32768] and a latent
+ * row of at most 16 KiB (d_latent <= 8192 in bf16, 4096 in f32), else LMOE_ERR_UNSUPPORTED. */
 
 enum { LMOE_CALL_ROUTE = 0, LMOE_CALL_PERMUTE = 1, LMOE_CALL_GROUPED_GLU = 2 };
 
@@ -153,10 +154,11 @@ lmoe_status lmoe_pack_shared(const lmoe_shape* shape, const void* w1s, const voi
  *   w_up         [D, L] act_dtype
  *   y_shared     [T, D] f32 or NULL       added before the final rounding
  *   n_out        [T, L] act_dtype (out)   n = gamma * z / sqrt(mean(z^2) + eps), z = sum_j w_tj y(t,j)
- *   out          [T, D] act_dtype (out)   n . w_up^T + y_shared                                    */
+ *   out          [T, D] out_dtype (out)   n . w_up^T + y_shared, rounded once from the f32
+ *                                         accumulator; out_dtype is LMOE_F32 or act_dtype           */
 lmoe_status lmoe_combine_norm_up(const lmoe_shape* shape, const void* y_perm, const int32_t* slot_of_pair,
                                  const float* topk_w, const float* gamma, const void* w_up,
-                                 const float* y_shared, void* n_out, void* out, void* stream);
+                                 const float* y_shared, void* n_out, void* out, int32_t out_dtype, void* stream);
 
 /* Kernel timing for measurement. When enabled, every kernel the library enqueues is bracketed by
  * HIP events on its stream. lmoe_profile_collect() synchronises those events and folds them into

@@ -67,7 +67,7 @@ def lib() -> ctypes.CDLL:
                                                      ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
                                                      ctypes.c_int32, _P, ctypes.c_size_t, _P]),
             "lmoe_pack_shared": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
-            "lmoe_combine_norm_up": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+            "lmoe_combine_norm_up": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P]),
             "lmoe_profile_enable": (None, [ctypes.c_int]),
             "lmoe_profile_reset": (None, []),
             "lmoe_profile_collect": (ctypes.c_int, []),
@@ -155,9 +155,10 @@ def lmoe_pack_shared(shape, w1s, w2s, w1s_packed, w2s_packed, stream=None):
 
 
 def lmoe_combine_norm_up(shape, y_perm, slot_of_pair, topk_w, gamma, w_up, y_shared, n_out, out, stream=None):
+    out_dtype = LMOE_F32 if out.dtype == torch.float32 else LMOE_BF16
     _check("lmoe_combine_norm_up",
            lib().lmoe_combine_norm_up(ctypes.byref(shape), _ptr(y_perm), _ptr(slot_of_pair), _ptr(topk_w),
-                                      _ptr(gamma), _ptr(w_up), _ptr(y_shared), _ptr(n_out), _ptr(out),
+                                      _ptr(gamma), _ptr(w_up), _ptr(y_shared), _ptr(n_out), _ptr(out), out_dtype,
                                       _stream(stream)))
 
 

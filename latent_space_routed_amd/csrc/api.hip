@@ -264,9 +264,10 @@ lmoe_status lmoe_pack_shared(const lmoe_shape* sh, const void* w1s, const void* 
 
 lmoe_status lmoe_combine_norm_up(const lmoe_shape* sh, const void* y_perm, const int32_t* slot_of_pair,
                                  const float* topk_w, const float* gamma, const void* w_up, const float* y_shared,
-                                 void* n_out, void* out, void* stream) {
+                                 void* n_out, void* out, int32_t out_dtype, void* stream) {
   lmoe_status st = check_shape(sh);
   if (st != LMOE_OK) return st;
+  if (out_dtype != LMOE_F32 && out_dtype != sh->act_dtype) return LMOE_ERR_INVALID_ARGUMENT;
   if (sh->T == 0) return LMOE_OK;
   if (!aligned16(y_perm) || !aligned4(slot_of_pair) || !aligned4(topk_w) || (gamma && !aligned4(gamma)) ||
       !aligned16(w_up) || (y_shared && !aligned4(y_shared)) || !aligned16(n_out) || !aligned16(out))
@@ -284,7 +285,7 @@ lmoe_status lmoe_combine_norm_up(const lmoe_shape* sh, const void* y_perm, const
   a.ldb = L;
   a.C = out;
   a.ldc = D;
-  a.c_dtype = sh->act_dtype;
+  a.c_dtype = out_dtype;
   a.M = T;
   a.N = D;
   a.K = L;

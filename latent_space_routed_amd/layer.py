@@ -30,8 +30,10 @@ def to_device(a: np.ndarray | None, act_dtype: str, device="cuda") -> torch.Tens
 class LatentMoE:
     """One layer instance: weights on the device, per-batch buffers sized for up to ``max_tokens``."""
 
-    def __init__(self, cfg, weights: dict, max_tokens: int | None = None, device: str = "cuda"):
+    def __init__(self, cfg, weights: dict, max_tokens: int | None = None, device: str = "cuda",
+                 out_dtype: torch.dtype = torch.float32):
         self.cfg = cfg
+        self.out_dtype = out_dtype
         self.device = device
         self.max_tokens = cfg.T if max_tokens is None else max_tokens
         self.w = weights
@@ -71,7 +73,7 @@ class LatentMoE:
             "h_s": torch.empty(T, max(S * Is, 64), dtype=dt, device=dev),
             "y_sh": torch.empty(T, D, dtype=f32, device=dev),
             "n": torch.empty(T, L, dtype=dt, device=dev),
-            "out": torch.empty(T, D, dtype=dt, device=dev),
+            "out": torch.empty(T, D, dtype=self.out_dtype, device=dev),
         }
         for name, which in (("ws_route", C.LMOE_CALL_ROUTE), ("ws_permute", C.LMOE_CALL_PERMUTE),
                             ("ws_glu", C.LMOE_CALL_GROUPED_GLU)):
