@@ -89,6 +89,8 @@ def main() -> int:
     ap.add_argument("--workload", default="k3_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=256)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB 5 times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -104,6 +106,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        return 0
     cfg = CONFIGS[args.workload]
     log(f"[bench] generating {cfg.name} inputs")
     t0 = time.perf_counter()

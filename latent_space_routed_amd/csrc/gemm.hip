@@ -20,6 +20,8 @@
 //    numbering is split into 8 contiguous ranges, one per XCD (workgroup i runs on XCD i mod 8):
 //    the m-tiles sharing an expert's weight slice, and the n-tiles sharing its rows, run together
 //    on one XCD and meet in its L2.
+#include <type_traits>
+
 #include "common.h"
 
 namespace lmoe {
@@ -50,6 +52,18 @@ struct Mfma<float> {
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.w, fb.w, acc, 0, 0, 0);
   }
 };
+
+// Raw buffer resource over [base, base + bytes): dword 3 = 0x00020000 is the gfx9-family raw
+// buffer format (32-bit data, no swizzle, offset-checked against num_records).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ inline uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ inline void store_out(const GemmArgs& p, int64_t off, float v) {
   if (p.c_dtype == LMOE_F32)
@@ -120,49 +134,46 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_kernel(GemmArgs 
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
   // ---------------------------------------------------------------- global -> LDS staging
-  const char* Ab = static_cast<const char*>(p.A);
-  const char* Bb = static_cast<const char*>(p.B) + (int64_t)g * p.b_gstride * (int64_t)sizeof(TI);
+  // Buffer resources span exactly the tile's valid rows of A and of B (one each for the gate and
+  // up halves of a GLU tile): a chunk past the end reads as zero in hardware, so ragged row and
+  // column tails need neither predication nor clamping. The K offset is the uniform soffset, so
+  // a lane's 32-bit voffsets stay fixed for the whole K loop.
   const int64_t a_ld = p.lda * (int64_t)sizeof(TI), b_ld = p.ldb * (int64_t)sizeof(TI);
+  const char* Ab = static_cast<const char*>(p.A) + (int64_t)row0 * a_ld;
+  const char* Bb = static_cast<const char*>(p.B) + (int64_t)g * p.b_gstride * (int64_t)sizeof(TI);
+  const int ncols = min(BNO, p.N - n0);
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(Ab, (int)(rows * a_ld));
+  const __amdgpu_buffer_rsrc_t b_rsrc0 = make_rsrc(Bb + (int64_t)n0 * b_ld, (int)(ncols * b_ld));
+  const __amdgpu_buffer_rsrc_t b_rsrc1 =
+      GLU ? make_rsrc(Bb + (int64_t)(p.glu_up_off + n0) * b_ld, (int)(ncols * b_ld)) : b_rsrc0;
   const int a_wrap = p.a_kwrap * (int)sizeof(TI);
   const int KT = p.K * (int)sizeof(TI) / 128;
+  static_assert(!GLU || BNO % (NT / 8) == 0, "a B chunk index must stay in one GLU half");
 
-  const char* a_src[A_PER];
-  const char* b_src[B_PER];
-  bool a_ok[A_PER], b_ok[B_PER];
+  int a_voff[A_PER], b_voff[B_PER];
 #pragma unroll
   for (int i = 0; i < A_PER; ++i) {
-    const int c = tid + i * NT, r = c >> 3, ch = c & 7;
-    a_ok[i] = r < rows;
-    a_src[i] = Ab + (a_ok[i] ? (int64_t)(row0 + r) * a_ld : 0) + ch * 16;
+    const int c = tid + i * NT;
+    a_voff[i] = (c >> 3) * (int)a_ld + (c & 7) * 16;
   }
 #pragma unroll
   for (int i = 0; i < B_PER; ++i) {
-    const int c = tid + i * NT, r = c >> 3, ch = c & 7;
-    int brow;
-    if (GLU) {
-      const int col = n0 + (r % BNO);
-      b_ok[i] = col < p.N;
-      brow = (r < BNO) ? col : p.glu_up_off + col;
-    } else {
-      brow = n0 + r;
-      b_ok[i] = brow < p.N;
-    }
-    b_src[i] = Bb + (b_ok[i] ? (int64_t)brow * b_ld : 0) + ch * 16;
+    const int c = tid + i * NT;
+    b_voff[i] = ((c >> 3) % BNO) * (int)b_ld + (c & 7) * 16;
   }
 
   uint4 ra[A_PER], rb[B_PER];
-  int ka = 0;  // byte offset of the current K-tile inside A's (possibly wrapped) row
-  auto gload = [&](int kt) {
+  int ka = 0;  // byte offset of the next K-tile inside A's (possibly wrapped) row
+  auto gload = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i)
-      ra[i] = a_ok[i] ? *reinterpret_cast<const uint4*>(a_src[i] + ka) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < A_PER; ++i) ra[i] = buffer_load16(a_rsrc, a_voff[i], ka);
 #pragma unroll
     for (int i = 0; i < B_PER; ++i)
-      rb[i] = b_ok[i] ? *reinterpret_cast<const uint4*>(b_src[i] + (int64_t)kt * 128) : make_uint4(0, 0, 0, 0);
+      rb[i] = buffer_load16((GLU && (i * NT / 8) >= BNO) ? b_rsrc1 : b_rsrc0, b_voff[i], kt * 128);
     ka += 128;
     if (ka == a_wrap) ka = 0;
   };
-  auto lstore = [&](int stage) {
+  auto lstore = [&](int stage) __attribute__((always_inline)) {
     char* base = smem + stage * STAGE;
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
@@ -185,41 +196,52 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_kernel(GemmArgs 
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
+  // The wave's row-blocks i * WAVES_M + wm that hold rows of the tile form a prefix i < na, so the
+  // K loop is instantiated per na, so no branch sits between the LDS reads and the MFMAs. Every
+  // column-block is computed; column tails are masked at the store.
+  const int na = min(WM, max(0, (act_rb - wm + WAVES_M - 1) / WAVES_M));
   const int frag_off = (lane & 31) * kRowPitch + (lane >> 5) * 16;
-  auto compute = [&](int stage) {
-    const char* base = smem + stage * STAGE;
+
+  auto main_loop = [&](auto na_c) __attribute__((always_inline)) {
+    constexpr int NA = decltype(na_c)::value;
+    auto compute = [&](int stage) __attribute__((always_inline)) {
+      const char* base = smem + stage * STAGE;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint4 af[WM], bf[WN];
+      for (int s = 0; s < 4; ++s) {
+        uint4 af[NA > 0 ? NA : 1], bf[WN];
 #pragma unroll
-      for (int i = 0; i < WM; ++i) {
-        const int rbk = i * WAVES_M + wm;
-        if (rbk < act_rb) af[i] = *reinterpret_cast<const uint4*>(base + rbk * 32 * kRowPitch + frag_off + s * 32);
-      }
+        for (int i = 0; i < NA; ++i)
+          af[i] = *reinterpret_cast<const uint4*>(base + (i * WAVES_M + wm) * 32 * kRowPitch + frag_off + s * 32);
 #pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const int ocb = (j % WNO) * WAVES_N + wn;
-        const int bblk = (GLU && j >= WNO) ? BNO / 32 + ocb : ocb;
-        if (ocb < act_cb)
+        for (int j = 0; j < WN; ++j) {
+          const int ocb = (j % WNO) * WAVES_N + wn;
+          const int bblk = (GLU && j >= WNO) ? BNO / 32 + ocb : ocb;
           bf[j] = *reinterpret_cast<const uint4*>(base + A_BYTES + bblk * 32 * kRowPitch + frag_off + s * 32);
+        }
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j) Mfma<TI>::run(acc[i][j], af[i], bf[j]);
       }
-#pragma unroll
-      for (int i = 0; i < WM; ++i)
-#pragma unroll
-        for (int j = 0; j < WN; ++j)
-          if (i * WAVES_M + wm < act_rb && (j % WNO) * WAVES_N + wn < act_cb) Mfma<TI>::run(acc[i][j], af[i], bf[j]);
+    };
+    // K-tile t sits in LDS stage t % 2; one barrier per K-tile.
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + 1 < KT) gload(kt + 1);
+      if (NA > 0) compute(kt & 1);
+      if (kt + 1 < KT) lstore((kt + 1) & 1);
+      __syncthreads();
     }
   };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    compute(cur);
-    if (kt + 1 < KT) lstore(cur ^ 1);
-    __syncthreads();
+  static_assert(WM <= 4, "main-loop specialisations cover up to four row-blocks per wave");
+  switch (na) {
+    case 0: main_loop(std::integral_constant<int, 0>{}); break;
+    case 1: main_loop(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (WM >= 2) main_loop(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (WM >= 3) main_loop(std::integral_constant<int, 3>{}); break;
+    default: if constexpr (WM >= 4) main_loop(std::integral_constant<int, 4>{}); break;
   }
 
   // ---------------------------------------------------------------- epilogue
