@@ -113,7 +113,15 @@ def main() -> int:
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        print(json.dumps({"copy_probe_bytes": n, "launches": 15, "ms_per_copy": ms,
+                          "read_plus_write_GBs": 2 * n / ms / 1e6}), flush=True)
         return 0
     cfg = CONFIGS[args.workload]
     log(f"[bench] generating {cfg.name} inputs")

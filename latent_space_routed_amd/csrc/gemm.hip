@@ -3,15 +3,27 @@
 //
 // Layout and schedule:
 //  * A and B are K-contiguous ("[out, in]" weights), so both MFMA operands are read as 16-byte
-//    chunks along K. A K-tile is 128 bytes of every row (64 bf16 or 32 f32), staged in LDS with a
-//    144-byte row pitch: eight lanes reading 16 bytes of eight consecutive rows then cover all 32
-//    banks, which keeps the ds_read_b128 fragment loads conflict-free.
-//  * Two LDS stages: global loads of K-tile t+1 are issued into registers before the MFMAs of
-//    K-tile t and written to the other stage afterwards, so one barrier per K-tile suffices.
+//    chunks along K: lane l of a 32x32x16 MFMA takes 8 k-values of row l % 32 (A) or column l % 32
+//    (B), the two lane halves covering the 16 k of the step.
 //  * Waves tile the block as WAVES_M x WAVES_N; a wave owns WM row-blocks and WN column-blocks of
 //    32x32 (v_mfma_f32_32x32x16_bf16, or four v_mfma_f32_32x32x2f32 for f32 data). Row-blocks are
-//    interleaved across the M-waves so a ragged tail spreads evenly, and row-blocks past the end of
-//    a group are skipped entirely (no loads, no MFMAs).
+//    interleaved across the M-waves so a ragged tail spreads evenly; a wave's row-blocks holding
+//    rows of the tile form a prefix, and the K loop is instantiated per prefix length, so no
+//    branch sits between the LDS reads and the MFMAs and empty row-blocks cost nothing.
+//  * Two pipelines:
+//    - DMA (256x256 tiles): K-tiles of 32 bf16 (64 bytes of each row) go straight from HBM into
+//      LDS with buffer_load ... lds, four LDS stages deep, so three K-tiles (96 KB per CU) are in
+//      flight while the MFMAs consume the fourth, without any register staging. A DMA instruction
+//      writes 64 lanes x 16 bytes contiguously (16 rows of 64 bytes); each lane fetches the chunk
+//      that belongs at its slot under an XOR swizzle (slot = chunk ^ ((row >> 1) & 3)), which makes
+//      the ds_read_b128 fragment reads of eight consecutive rows hit eight distinct bank groups.
+//      The DMA is issued from inline assembly with its own vmcnt waits, because the compiler's
+//      waitcnt pass would otherwise drain every outstanding DMA before each LDS read.
+//    - Registers (128x128 tiles): K-tiles of 128 bytes per row are loaded into registers one
+//      K-tile ahead and written to one of two padded LDS stages (144-byte pitch, conflict-free).
+//  * Global loads use buffer resources that span exactly the tile's valid rows of A and of B (one
+//    each for the gate and up halves of a GLU tile): past the end a load returns zero, so ragged
+//    row and column tails need no predication. The K offset rides in the uniform soffset.
 //  * The GLU epilogue needs gate column c and up column c in the same lane: a wave's first WN/2
 //    column-blocks read gate rows of B and its last WN/2 the matching up rows, so the MFMA result
 //    layouts coincide and SiTU-GLU is applied in registers (unfused it costs an extra pass over
@@ -27,7 +39,7 @@
 namespace lmoe {
 namespace {
 
-constexpr int kRowPitch = 144;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename TI>
 struct Mfma;
@@ -53,16 +65,40 @@ struct Mfma<float> {
   }
 };
 
-// Raw buffer resource over [base, base + bytes): dword 3 = 0x00020000 is the gfx9-family raw
-// buffer format (32-bit data, no swizzle, offset-checked against num_records).
+// Raw buffer descriptor over [base, base + bytes): word 3 = 0x00020000 is the gfx9-family raw
+// buffer format (32-bit data, no swizzle); reads past num_records return zero.
+constexpr unsigned kBufWord3 = 0x00020000u;
+
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufWord3);
+}
+
+__device__ inline u32x4 make_desc(const void* base, int bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  u32x4 d;
+  d.x = __builtin_amdgcn_readfirstlane((unsigned)a);
+  d.y = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xffffu);  // stride 0
+  d.z = __builtin_amdgcn_readfirstlane((unsigned)bytes);
+  d.w = kBufWord3;
+  return d;
 }
 
 __device__ inline uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// One wave-wide DMA: lane i's 16 bytes from desc + voff + soff land at LDS lds_addr + 16 i.
+__device__ inline void dma16(const u32x4& desc, int voff, int soff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(desc), "s"(soff)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
 __device__ inline void store_out(const GemmArgs& p, int64_t off, float v) {
@@ -72,34 +108,26 @@ __device__ inline void store_out(const GemmArgs& p, int64_t off, float v) {
     static_cast<uint16_t*>(p.C)[off] = f32_to_bf16(v);
 }
 
-template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, Epi EPI>
-__global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_kernel(GemmArgs p) {
-  constexpr int NT = WAVES_M * WAVES_N * kWave;
-  constexpr int BM = WAVES_M * WM * 32;
-  constexpr int BNB = WAVES_N * WN * 32;  // rows of B per tile
-  constexpr bool GLU = EPI == Epi::Glu;
-  static_assert(!GLU || WN % 2 == 0, "GLU needs gate/up column-block pairs");
-  constexpr int BNO = GLU ? BNB / 2 : BNB;  // output columns per tile
-  constexpr int WNO = GLU ? WN / 2 : WN;    // output column-blocks per wave
-  constexpr int A_PER = BM * 8 / NT;
-  constexpr int B_PER = BNB * 8 / NT;
-  static_assert(A_PER * NT == BM * 8 && B_PER * NT == BNB * 8, "chunk split");
-  constexpr int A_BYTES = BM * kRowPitch;
-  constexpr int STAGE = (BM + BNB) * kRowPitch;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+// ------------------------------------------------------------------------------------------------
+// tile assignment and epilogue shared by both pipelines
+// ------------------------------------------------------------------------------------------------
+struct TileInfo {
+  int g, n0, row0, rows;
+};
 
-  // ---------------------------------------------------------------- tile assignment
+template <int BM, int BNO>
+__device__ inline bool assign_tile(const GemmArgs& p, TileInfo& t) {
   const bool grouped = p.goff != nullptr;
   const int n_tiles = (int)ceil_div(p.N, BNO);
   const int mt_total = grouped ? p.mtile_start[p.G] : (int)ceil_div(p.M, BM);
   const int total = mt_total * n_tiles;
   const int per = (total + kXcds - 1) / kXcds;
   const int loc = blockIdx.x / kXcds;
-  if (loc >= per) return;
+  if (loc >= per) return false;
   const int lt = (blockIdx.x % kXcds) * per + loc;
-  if (lt >= total) return;
-
-  int g = 0, n_tile, row0, rows;
+  if (lt >= total) return false;
+  int n_tile;
+  t.g = 0;
   if (grouped) {
     const int q = lt / n_tiles;
     int lo = 0, hi = p.G;  // mtile_start[lo] <= q < mtile_start[hi]
@@ -107,48 +135,243 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_kernel(GemmArgs 
       const int mid = (lo + hi) >> 1;
       if (p.mtile_start[mid] <= q) lo = mid; else hi = mid;
     }
-    g = lo;
-    const int ms0 = p.mtile_start[g];
-    const int mtg = p.mtile_start[g + 1] - ms0;
+    t.g = lo;
+    const int ms0 = p.mtile_start[lo];
+    const int mtg = p.mtile_start[lo + 1] - ms0;
     const int r = lt - n_tiles * ms0;
     n_tile = r / mtg;
-    const int m_tile = r % mtg;
-    row0 = p.goff[g] + m_tile * BM;
-    rows = min(BM, p.goff[g + 1] - row0);
+    t.row0 = p.goff[lo] + (r % mtg) * BM;
+    t.rows = min(BM, p.goff[lo + 1] - t.row0);
   } else {
     constexpr int GM = 8;  // raster: 8 m-tiles x all n-tiles, m fastest
     const int MT = (int)ceil_div(p.M, BM);
     const int gsz = GM * n_tiles;
     const int grp = lt / gsz, first = grp * GM, gm = min(MT - first, GM), r = lt % gsz;
     n_tile = r / gm;
-    row0 = (first + r % gm) * BM;
-    rows = min(BM, p.M - row0);
+    t.row0 = (first + r % gm) * BM;
+    t.rows = min(BM, p.M - t.row0);
   }
-  const int n0 = n_tile * BNO;
-  const int act_rb = (rows + 31) >> 5;
-  const int act_cb = (min(BNO, p.N - n0) + 31) >> 5;
+  t.n0 = n_tile * BNO;
+  return true;
+}
 
+template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, Epi EPI>
+__device__ inline void epilogue(const GemmArgs& p, const TileInfo& t, f32x16 (&acc)[WM][WN], int wm, int wn,
+                                int lane, int na) {
+  constexpr bool GLU = EPI == Epi::Glu;
+  constexpr int WNO = GLU ? WN / 2 : WN;
+  const float inv_b1 = 1.0f / p.beta1, inv_b2 = 1.0f / p.beta2;
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    if (i >= na) continue;
+    const int rbk = i * WAVES_M + wm;
+#pragma unroll
+    for (int j = 0; j < WNO; ++j) {
+      const int col = t.n0 + (j * WAVES_N + wn) * 32 + (lane & 31);
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = rbk * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        if (r >= t.rows) continue;
+        const int64_t grow = t.row0 + r;
+        const int64_t off = grow * p.ldc + col;
+        if constexpr (EPI == Epi::Store) {
+          store_out(p, off, acc[i][j][q]);
+        } else if constexpr (EPI == Epi::Glu) {
+          store_out(p, off, situ_glu<sizeof(TI) == 4>(acc[i][j][q], acc[i][j + WNO][q], p.beta1, inv_b1, p.beta2,
+                                                      inv_b2));
+        } else if constexpr (EPI == Epi::Sigmoid) {
+          const float v = acc[i][j][q] + (p.col_bias ? p.col_bias[col] : 0.0f);
+          static_cast<float*>(p.C)[off] = 1.0f / (1.0f + expf(-v));
+        } else {
+          store_out(p, off, acc[i][j][q] + p.residual[grow * p.ldr + col]);
+        }
+      }
+    }
+  }
+}
+
+template <int WM, int WN>
+__device__ inline void zero_acc(f32x16 (&acc)[WM][WN]) {
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
+#pragma unroll
+    for (int j = 0; j < WN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+}
+
+// Calls f(integral_constant<NA>) for the wave's active row-block count na (0..WM).
+template <int WM, typename F>
+__device__ inline void dispatch_na(int na, F&& f) {
+  static_assert(WM <= 4, "specialisations cover up to four row-blocks per wave");
+  switch (na) {
+    case 0: f(std::integral_constant<int, 0>{}); break;
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (WM >= 2) f(std::integral_constant<int, 2>{}); break;
+    case 3: if constexpr (WM >= 3) f(std::integral_constant<int, 3>{}); break;
+    default: if constexpr (WM >= 4) f(std::integral_constant<int, 4>{}); break;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// DMA pipeline: 256x256 tiles, LDS fed straight from HBM, three K-tiles in flight
+// ------------------------------------------------------------------------------------------------
+template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, Epi EPI>
+__global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_dma_kernel(GemmArgs p) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int BM = WAVES_M * WM * 32;
+  constexpr int BNB = WAVES_N * WN * 32;  // rows of B per tile
+  constexpr bool GLU = EPI == Epi::Glu;
+  static_assert(!GLU || WN % 2 == 0, "GLU needs gate/up column-block pairs");
+  constexpr int BNO = GLU ? BNB / 2 : BNB;
+  constexpr int WNO = GLU ? WN / 2 : WN;
+  constexpr int NS = 4;                    // LDS stages
+  constexpr int KB = 64;                   // bytes of every row per K-tile
+  constexpr int RPD = 1024 / KB;           // rows per 1 KB DMA block
+  constexpr int A_PW = BM / RPD / NW;      // DMA blocks per wave per K-tile
+  constexpr int B_PW = BNB / RPD / NW;
+  static_assert(A_PW * RPD * NW == BM && B_PW * RPD * NW == BNB, "DMA split");
+  static_assert(!GLU || BNO % RPD == 0, "a DMA block stays in one GLU half");
+  constexpr int A_BYTES = BM * KB;
+  constexpr int STAGE = (BM + BNB) * KB;
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+
+  TileInfo t;
+  if (!assign_tile<BM, BNO>(p, t)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int na = min(WM, max(0, (((t.rows + 31) >> 5) - wm + WAVES_M - 1) / WAVES_M));
+
+  const int64_t a_ld = p.lda * (int64_t)sizeof(TI), b_ld = p.ldb * (int64_t)sizeof(TI);
+  const char* Bb = static_cast<const char*>(p.B) + (int64_t)t.g * p.b_gstride * (int64_t)sizeof(TI);
+  const int ncols = min(BNO, p.N - t.n0);
+  const u32x4 a_desc = make_desc(static_cast<const char*>(p.A) + (int64_t)t.row0 * a_ld, (int)(t.rows * a_ld));
+  const u32x4 b_desc0 = make_desc(Bb + (int64_t)t.n0 * b_ld, (int)(ncols * b_ld));
+  const u32x4 b_desc1 = GLU ? make_desc(Bb + (int64_t)(p.glu_up_off + t.n0) * b_ld, (int)(ncols * b_ld)) : b_desc0;
+  const int a_wrap = p.a_kwrap * (int)sizeof(TI);
+  const int KT = p.K * (int)sizeof(TI) / KB;
+
+  // The lane's source chunk for each DMA block of this wave (swizzled so that LDS slot s of row r
+  // holds chunk s ^ ((r >> 1) & 3)).
+  const int lr = lane >> 2, slot = lane & 3;
+  int a_voff[A_PW], b_voff[B_PW];
+#pragma unroll
+  for (int i = 0; i < A_PW; ++i) {
+    const int r = (wave * A_PW + i) * RPD + lr;
+    a_voff[i] = r * (int)a_ld + ((slot ^ ((r >> 1) & 3)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < B_PW; ++i) {
+    const int r = (wave * B_PW + i) * RPD + lr;
+    b_voff[i] = (r % BNO) * (int)b_ld + ((slot ^ ((r >> 1) & 3)) * 16);
+  }
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
+
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    const int ka = (kt * KB) % a_wrap;
+    const unsigned base = lds0 + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) dma16(a_desc, a_voff[i], ka, base + (wave * A_PW + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_PW; ++i) {
+      const bool up = GLU && (wave * B_PW + i) * RPD >= BNO;
+      dma16(up ? b_desc1 : b_desc0, b_voff[i], kt * KB, base + A_BYTES + (wave * B_PW + i) * 1024);
+    }
+  };
+  constexpr int PER_TILE = A_PW + B_PW;  // DMA instructions per wave per K-tile
+  auto wait_tiles_after = [&](int n) __attribute__((always_inline)) {
+    static_assert(NS == 4, "waits below cover up to two younger K-tiles");
+    if (n >= 2) wait_vmcnt<2 * PER_TILE>();
+    else if (n == 1) wait_vmcnt<PER_TILE>();
+    else wait_vmcnt<0>();
+  };
+
+  f32x16 acc[WM][WN];
+  zero_acc(acc);
+  // fragment offsets for the two 32-byte k-steps of a K-tile (row-block base added per block)
+  const int sw = ((lane & 31) >> 1) & 3;
+  const int fo0 = (lane & 31) * KB + (((lane >> 5) ^ sw) * 16);
+  const int fo1 = (lane & 31) * KB + (((2 + (lane >> 5)) ^ sw) * 16);
+
+  dispatch_na<WM>(na, [&](auto na_c) __attribute__((always_inline)) {
+    constexpr int NA = decltype(na_c)::value;
+    auto compute = [&](int stage) __attribute__((always_inline)) {
+      const char* base = smem + stage * STAGE;
+#pragma unroll
+      for (int s = 0; s < KB / 32; ++s) {
+        const int fo = s == 0 ? fo0 : fo1;
+        uint4 af[NA > 0 ? NA : 1], bf[WN];
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+          af[i] = *reinterpret_cast<const uint4*>(base + (i * WAVES_M + wm) * 32 * KB + fo);
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const int ocb = (j % WNO) * WAVES_N + wn;
+          const int bblk = (GLU && j >= WNO) ? BNO / 32 + ocb : ocb;
+          bf[j] = *reinterpret_cast<const uint4*>(base + A_BYTES + bblk * 32 * KB + fo);
+        }
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+          for (int j = 0; j < WN; ++j) Mfma<TI>::run(acc[i][j], af[i], bf[j]);
+      }
+    };
+    const int pre = min(KT, NS - 1);
+    for (int kt = 0; kt < pre; ++kt) issue(kt, kt);
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_tiles_after(min(KT - kt - 1, NS - 2));  // K-tile kt has landed in LDS (this wave's part)
+      __syncthreads();                             // ... and every wave's; stage kt-1 is free again
+      if (kt + NS - 1 < KT) issue(kt + NS - 1, (kt + NS - 1) % NS);
+      if (NA > 0) compute(kt % NS);
+    }
+  });
+  epilogue<TI, WAVES_M, WAVES_N, WM, WN, EPI>(p, t, acc, wm, wn, lane, na);
+}
+
+// ------------------------------------------------------------------------------------------------
+// register pipeline: 128x128 tiles, one K-tile of loads in flight, two padded LDS stages
+// ------------------------------------------------------------------------------------------------
+constexpr int kRowPitch = 144;
+
+template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, Epi EPI>
+__global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_reg_kernel(GemmArgs p) {
+  constexpr int NT = WAVES_M * WAVES_N * kWave;
+  constexpr int BM = WAVES_M * WM * 32;
+  constexpr int BNB = WAVES_N * WN * 32;
+  constexpr bool GLU = EPI == Epi::Glu;
+  static_assert(!GLU || WN % 2 == 0, "GLU needs gate/up column-block pairs");
+  constexpr int BNO = GLU ? BNB / 2 : BNB;
+  constexpr int WNO = GLU ? WN / 2 : WN;
+  constexpr int A_PER = BM * 8 / NT;
+  constexpr int B_PER = BNB * 8 / NT;
+  static_assert(A_PER * NT == BM * 8 && B_PER * NT == BNB * 8, "chunk split");
+  static_assert(!GLU || BNO % (NT / 8) == 0, "a B chunk index must stay in one GLU half");
+  constexpr int A_BYTES = BM * kRowPitch;
+  constexpr int STAGE = (BM + BNB) * kRowPitch;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  TileInfo t;
+  if (!assign_tile<BM, BNO>(p, t)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int na = min(WM, max(0, (((t.rows + 31) >> 5) - wm + WAVES_M - 1) / WAVES_M));
 
-  // ---------------------------------------------------------------- global -> LDS staging
-  // Buffer resources span exactly the tile's valid rows of A and of B (one each for the gate and
-  // up halves of a GLU tile): a chunk past the end reads as zero in hardware, so ragged row and
-  // column tails need neither predication nor clamping. The K offset is the uniform soffset, so
-  // a lane's 32-bit voffsets stay fixed for the whole K loop.
   const int64_t a_ld = p.lda * (int64_t)sizeof(TI), b_ld = p.ldb * (int64_t)sizeof(TI);
-  const char* Ab = static_cast<const char*>(p.A) + (int64_t)row0 * a_ld;
-  const char* Bb = static_cast<const char*>(p.B) + (int64_t)g * p.b_gstride * (int64_t)sizeof(TI);
-  const int ncols = min(BNO, p.N - n0);
-  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(Ab, (int)(rows * a_ld));
-  const __amdgpu_buffer_rsrc_t b_rsrc0 = make_rsrc(Bb + (int64_t)n0 * b_ld, (int)(ncols * b_ld));
+  const char* Bb = static_cast<const char*>(p.B) + (int64_t)t.g * p.b_gstride * (int64_t)sizeof(TI);
+  const int ncols = min(BNO, p.N - t.n0);
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      make_rsrc(static_cast<const char*>(p.A) + (int64_t)t.row0 * a_ld, (int)(t.rows * a_ld));
+  const __amdgpu_buffer_rsrc_t b_rsrc0 = make_rsrc(Bb + (int64_t)t.n0 * b_ld, (int)(ncols * b_ld));
   const __amdgpu_buffer_rsrc_t b_rsrc1 =
-      GLU ? make_rsrc(Bb + (int64_t)(p.glu_up_off + n0) * b_ld, (int)(ncols * b_ld)) : b_rsrc0;
+      GLU ? make_rsrc(Bb + (int64_t)(p.glu_up_off + t.n0) * b_ld, (int)(ncols * b_ld)) : b_rsrc0;
   const int a_wrap = p.a_kwrap * (int)sizeof(TI);
   const int KT = p.K * (int)sizeof(TI) / 128;
-  static_assert(!GLU || BNO % (NT / 8) == 0, "a B chunk index must stay in one GLU half");
 
   int a_voff[A_PER], b_voff[B_PER];
 #pragma unroll
@@ -187,22 +410,10 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_kernel(GemmArgs 
     }
   };
 
-  // ---------------------------------------------------------------- MFMA main loop
   f32x16 acc[WM][WN];
-#pragma unroll
-  for (int i = 0; i < WM; ++i)
-#pragma unroll
-    for (int j = 0; j < WN; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
-  // The wave's row-blocks i * WAVES_M + wm that hold rows of the tile form a prefix i < na, so the
-  // K loop is instantiated per na, so no branch sits between the LDS reads and the MFMAs. Every
-  // column-block is computed; column tails are masked at the store.
-  const int na = min(WM, max(0, (act_rb - wm + WAVES_M - 1) / WAVES_M));
+  zero_acc(acc);
   const int frag_off = (lane & 31) * kRowPitch + (lane >> 5) * 16;
-
-  auto main_loop = [&](auto na_c) __attribute__((always_inline)) {
+  dispatch_na<WM>(na, [&](auto na_c) __attribute__((always_inline)) {
     constexpr int NA = decltype(na_c)::value;
     auto compute = [&](int stage) __attribute__((always_inline)) {
       const char* base = smem + stage * STAGE;
@@ -224,7 +435,6 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_kernel(GemmArgs 
           for (int j = 0; j < WN; ++j) Mfma<TI>::run(acc[i][j], af[i], bf[j]);
       }
     };
-    // K-tile t sits in LDS stage t % 2; one barrier per K-tile.
     gload(0);
     lstore(0);
     __syncthreads();
@@ -234,67 +444,49 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_kernel(GemmArgs 
       if (kt + 1 < KT) lstore((kt + 1) & 1);
       __syncthreads();
     }
-  };
-  static_assert(WM <= 4, "main-loop specialisations cover up to four row-blocks per wave");
-  switch (na) {
-    case 0: main_loop(std::integral_constant<int, 0>{}); break;
-    case 1: main_loop(std::integral_constant<int, 1>{}); break;
-    case 2: if constexpr (WM >= 2) main_loop(std::integral_constant<int, 2>{}); break;
-    case 3: if constexpr (WM >= 3) main_loop(std::integral_constant<int, 3>{}); break;
-    default: if constexpr (WM >= 4) main_loop(std::integral_constant<int, 4>{}); break;
-  }
-
-  // ---------------------------------------------------------------- epilogue
-  const float inv_b1 = 1.0f / p.beta1, inv_b2 = 1.0f / p.beta2;
-#pragma unroll
-  for (int i = 0; i < WM; ++i) {
-    const int rbk = i * WAVES_M + wm;
-    if (rbk >= act_rb) continue;
-#pragma unroll
-    for (int j = 0; j < WNO; ++j) {
-      const int ocb = j * WAVES_N + wn;
-      if (ocb >= act_cb) continue;
-      const int col = n0 + ocb * 32 + (lane & 31);
-      if (col >= p.N) continue;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r = rbk * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        if (r >= rows) continue;
-        const int64_t grow = row0 + r;
-        const int64_t off = grow * p.ldc + col;
-        if constexpr (EPI == Epi::Store) {
-          store_out(p, off, acc[i][j][q]);
-        } else if constexpr (EPI == Epi::Glu) {
-          store_out(p, off, situ_glu<sizeof(TI) == 4>(acc[i][j][q], acc[i][j + WNO][q], p.beta1, inv_b1, p.beta2, inv_b2));
-        } else if constexpr (EPI == Epi::Sigmoid) {
-          const float v = acc[i][j][q] + (p.col_bias ? p.col_bias[col] : 0.0f);
-          static_cast<float*>(p.C)[off] = 1.0f / (1.0f + expf(-v));
-        } else {
-          store_out(p, off, acc[i][j][q] + p.residual[grow * p.ldr + col]);
-        }
-      }
-    }
-  }
+  });
+  epilogue<TI, WAVES_M, WAVES_N, WM, WN, EPI>(p, t, acc, wm, wn, lane, na);
 }
 
-template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN>
-hipError_t launch_shape(const GemmArgs& a, Epi epi, hipStream_t s) {
-  constexpr int BM = WAVES_M * WM * 32, BNB = WAVES_N * WN * 32;
+// ------------------------------------------------------------------------------------------------
+// launch
+// ------------------------------------------------------------------------------------------------
+template <int BM, int BNB>
+int64_t grid_blocks(const GemmArgs& a, Epi epi) {
   const int bno = epi == Epi::Glu ? BNB / 2 : BNB;
   const int64_t n_tiles = ceil_div(a.N, bno);
   const int64_t m_tiles = a.goff ? (int64_t)a.M / BM + a.G : ceil_div(a.M, BM);  // upper bound if grouped
-  const int64_t blocks = ceil_div(m_tiles * n_tiles, kXcds) * kXcds;
+  return ceil_div(m_tiles * n_tiles, kXcds) * kXcds;
+}
+
+#define LMOE_LAUNCH_EPI(KERNEL, ...)                                                                              \
+  switch (epi) {                                                                                                  \
+    case Epi::Store: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, Epi::Store>), grid, block, 0, s, a); break;         \
+    case Epi::Glu: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, Epi::Glu>), grid, block, 0, s, a); break;             \
+    case Epi::Sigmoid: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, Epi::Sigmoid>), grid, block, 0, s, a); break;     \
+    case Epi::AddF32: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, Epi::AddF32>), grid, block, 0, s, a); break;       \
+  }
+
+template <typename TI>
+hipError_t launch_big(const GemmArgs& a, Epi epi, hipStream_t s) {
+  const int64_t blocks = grid_blocks<256, 256>(a, epi);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(WAVES_M * WAVES_N * kWave);
-  switch (epi) {
-    case Epi::Store: hipLaunchKernelGGL((gemm_kernel<TI, WAVES_M, WAVES_N, WM, WN, Epi::Store>), grid, block, 0, s, a); break;
-    case Epi::Glu: hipLaunchKernelGGL((gemm_kernel<TI, WAVES_M, WAVES_N, WM, WN, Epi::Glu>), grid, block, 0, s, a); break;
-    case Epi::Sigmoid: hipLaunchKernelGGL((gemm_kernel<TI, WAVES_M, WAVES_N, WM, WN, Epi::Sigmoid>), grid, block, 0, s, a); break;
-    case Epi::AddF32: hipLaunchKernelGGL((gemm_kernel<TI, WAVES_M, WAVES_N, WM, WN, Epi::AddF32>), grid, block, 0, s, a); break;
-  }
+  const dim3 grid((unsigned)blocks), block(8 * kWave);
+  LMOE_LAUNCH_EPI(gemm_dma_kernel, TI, 2, 4, 4, 2)
   return hipGetLastError();
 }
+
+template <typename TI>
+hipError_t launch_small(const GemmArgs& a, Epi epi, hipStream_t s) {
+  const int64_t blocks = grid_blocks<128, 128>(a, epi);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(4 * kWave);
+  LMOE_LAUNCH_EPI(gemm_reg_kernel, TI, 2, 2, 2, 2)
+  return hipGetLastError();
+}
+#undef LMOE_LAUNCH_EPI
 
 // Exclusive prefix of ceil(n_g / bm) over groups: m-tile numbering of a grouped GEMM.
 __global__ void __launch_bounds__(1024) mtile_prefix_kernel(const int32_t* goff, int G, int bm, int32_t* ms) {
@@ -327,12 +519,9 @@ int gemm_block_m(GemmShape shape) { return shape == GemmShape::Big ? 256 : 128; 
 
 hipError_t launch_gemm(const GemmArgs& a, int in_dtype, Epi epi, GemmShape shape, hipStream_t s) {
   KernelTimer timer(a.tag ? a.tag : "gemm", s);
-  if (in_dtype == LMOE_BF16) {
-    if (shape == GemmShape::Big) return launch_shape<uint16_t, 2, 4, 4, 2>(a, epi, s);
-    return launch_shape<uint16_t, 2, 2, 2, 2>(a, epi, s);
-  }
-  if (shape == GemmShape::Big) return launch_shape<float, 2, 4, 4, 2>(a, epi, s);
-  return launch_shape<float, 2, 2, 2, 2>(a, epi, s);
+  if (in_dtype == LMOE_BF16)
+    return shape == GemmShape::Big ? launch_big<uint16_t>(a, epi, s) : launch_small<uint16_t>(a, epi, s);
+  return shape == GemmShape::Big ? launch_big<float>(a, epi, s) : launch_small<float>(a, epi, s);
 }
 
 hipError_t launch_mtile_prefix(const int32_t* goff, int G, int bm, int32_t* mtile_start, hipStream_t s) {
