@@ -109,7 +109,8 @@ lmoe_status lmoe_qb_update(const lmoe_shape* shape, uint32_t* hist, int64_t n_ac
  *   expert_offsets [E + 1] i32 (out)        first sorted row of each expert; [E] = T*k
  *   sorted_token   [T*k] i32 (out)          token of each sorted row (tokens ascending per expert)
  *   slot_of_pair   [T*k] i32 (out)          sorted row of pair t*k + j
- *   x_perm         [T*k, L] act_dtype (out) x_lat[sorted_token[r]]
+ *   x_perm         [T*k, L] act_dtype (out) x_lat[sorted_token[r]], or NULL to skip the copy (the
+ *                                           routed GEMM can read x_lat through sorted_token)
  *   workspace      LMOE_CALL_PERMUTE bytes                                                         */
 lmoe_status lmoe_permute(const lmoe_shape* shape, const void* x, const void* w_down, const int32_t* topk_idx,
                          void* x_lat, int32_t* expert_offsets, int32_t* sorted_token, int32_t* slot_of_pair,
@@ -119,22 +120,28 @@ lmoe_status lmoe_permute(const lmoe_shape* shape, const void* x, const void* w_d
  * [tahou] SiTU激活优化 and [slm] SiTU 激活: gate = first half of the first projection, up = second
  * half; h = beta1*tanh(g/beta1)*sigmoid(g) * beta2*tanh(u/beta2) in f32, fused in the epilogue.
  * For group g with rows [off[g], off[g+1]):
- *   [g | u] = a[rows] . w1[g]^T ;  h[rows] = SiTU-GLU ;  y[rows] = h[rows] . w2[g]^T
+ *   [g | u] = A[rows] . w1[g]^T ;  h[rows] = SiTU-GLU ;  y[rows] = h[rows] . w2[g]^T
+ * where row r of A is a[a_row_index[r]] (dispatch by gather: a = x_lat, a_row_index = sorted_token
+ * from lmoe_permute), or a[r] when a_row_index is NULL. A gathered index outside [0, a_rows) reads
+ * as a zero row.
  *   n_groups      G >= 1
- *   rows          total rows of a, h, y (= group_offsets[G])
+ *   rows          total rows of h and y (= group_offsets[G])
  *   K             input width (multiple of 64), inter: inner size (multiple of 64),
- *   n_out         output width (multiple of 32)
- *   a             [rows, K] act_dtype
+ *   n_out         output width
+ *   a             [a_rows, K] act_dtype; a_rows must equal rows when a_row_index is NULL
+ *   a_row_index   [rows] i32 device, or NULL
  *   group_offsets [G + 1] i32 device, non-decreasing, [0] = 0; NULL means one group of all rows
  *   w1            [G, 2*inter, K] act_dtype (gate rows 0..inter-1, up rows inter..2*inter-1)
- *   w2            [G, n_out, inter] act_dtype
+ *   w2            [G, n_out, inter] act_dtype, or NULL to stop after h (y is then unused)
  *   h             [rows, inter] act_dtype (out)
  *   y             [rows, n_out] y_dtype (out; y_dtype is LMOE_F32 or act_dtype)
- *   workspace     LMOE_CALL_GROUPED_GLU bytes (device tile list)                                 */
+ *   workspace     LMOE_CALL_GROUPED_GLU bytes (device tile list)
+ * With a_row_index, a must be under 2 GiB (31-bit byte offsets; LMOE_ERR_UNSUPPORTED otherwise). */
 lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* shape, int32_t n_groups, int32_t rows, int32_t K,
-                                  int32_t inter, int32_t n_out, const void* a, const int32_t* group_offsets,
-                                  const void* w1, const void* w2, void* h, void* y, int32_t y_dtype,
-                                  void* workspace, size_t workspace_bytes, void* stream);
+                                  int32_t inter, int32_t n_out, const void* a, int32_t a_rows,
+                                  const int32_t* a_row_index, const int32_t* group_offsets, const void* w1,
+                                  const void* w2, void* h, void* y, int32_t y_dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* Shared experts as one FFN ([vxz] 01: always-on shared experts; by linearity S SiTU-GLU experts
  * equal one of inner size S*I_s with the gate blocks, up blocks and down blocks concatenated).
@@ -152,13 +159,18 @@ lmoe_status lmoe_pack_shared(const lmoe_shape* shape, const void* w1s, const voi
  *   topk_w       [T, k] f32
  *   gamma        [L] f32 or NULL (= ones)
  *   w_up         [D, L] act_dtype
- *   y_shared     [T, D] f32 or NULL       added before the final rounding
+ *   shared part, at most one of:
+ *     y_shared   [T, D] f32               the shared experts' output, added before the final rounding
+ *     h_shared + w2_shared                their inner activations [T, S*I_s] and packed down weights
+ *                                         [D, S*I_s] (lmoe_pack_shared): out = [n | h_s] . [w_up |
+ *                                         w2_shared]^T accumulates both products in one f32 sum
  *   n_out        [T, L] act_dtype (out)   n = gamma * z / sqrt(mean(z^2) + eps), z = sum_j w_tj y(t,j)
- *   out          [T, D] out_dtype (out)   n . w_up^T + y_shared, rounded once from the f32
+ *   out          [T, D] out_dtype (out)   n . w_up^T + shared part, rounded once from the f32
  *                                         accumulator; out_dtype is LMOE_F32 or act_dtype           */
 lmoe_status lmoe_combine_norm_up(const lmoe_shape* shape, const void* y_perm, const int32_t* slot_of_pair,
                                  const float* topk_w, const float* gamma, const void* w_up,
-                                 const float* y_shared, void* n_out, void* out, int32_t out_dtype, void* stream);
+                                 const float* y_shared, const void* h_shared, const void* w2_shared,
+                                 void* n_out, void* out, int32_t out_dtype, void* stream);
 
 /* Kernel timing for measurement. When enabled, every kernel the library enqueues is bracketed by
  * HIP events on its stream. lmoe_profile_collect() synchronises those events and folds them into

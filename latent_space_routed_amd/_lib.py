@@ -64,10 +64,11 @@ def lib() -> ctypes.CDLL:
             "lmoe_qb_update": (ctypes.c_int, [_S, _P, ctypes.c_int64, _P, _P]),
             "lmoe_permute": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "lmoe_grouped_situ_glu": (ctypes.c_int, [_S, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                                     ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
-                                                     ctypes.c_int32, _P, ctypes.c_size_t, _P]),
+                                                     ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P,
+                                                     _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
             "lmoe_pack_shared": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
-            "lmoe_combine_norm_up": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P]),
+            "lmoe_combine_norm_up": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                                    _P]),
             "lmoe_profile_enable": (None, [ctypes.c_int]),
             "lmoe_profile_reset": (None, []),
             "lmoe_profile_collect": (ctypes.c_int, []),
@@ -141,12 +142,14 @@ def lmoe_permute(shape, x, w_down, topk_idx, x_lat, expert_offsets, sorted_token
 
 
 def lmoe_grouped_situ_glu(shape, n_groups: int, rows: int, K: int, inter: int, n_out: int, a, group_offsets, w1, w2,
-                          h, y, workspace, stream=None):
-    y_dtype = LMOE_F32 if y.dtype == torch.float32 else LMOE_BF16
+                          h, y, workspace, a_row_index=None, stream=None):
+    """a_row_index (optional): GEMM row r reads a[a_row_index[r]]; w2/y None stops after h."""
+    y_dtype = LMOE_F32 if (y is not None and y.dtype == torch.float32) else LMOE_BF16
+    a_rows = a.shape[0] if a_row_index is not None else rows
     _check("lmoe_grouped_situ_glu",
-           lib().lmoe_grouped_situ_glu(ctypes.byref(shape), n_groups, rows, K, inter, n_out, _ptr(a),
-                                       _ptr(group_offsets), _ptr(w1), _ptr(w2), _ptr(h), _ptr(y), y_dtype,
-                                       _ptr(workspace), _nbytes(workspace), _stream(stream)))
+           lib().lmoe_grouped_situ_glu(ctypes.byref(shape), n_groups, rows, K, inter, n_out, _ptr(a), a_rows,
+                                       _ptr(a_row_index), _ptr(group_offsets), _ptr(w1), _ptr(w2), _ptr(h), _ptr(y),
+                                       y_dtype, _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def lmoe_pack_shared(shape, w1s, w2s, w1s_packed, w2s_packed, stream=None):
@@ -154,12 +157,13 @@ def lmoe_pack_shared(shape, w1s, w2s, w1s_packed, w2s_packed, stream=None):
                                                       _ptr(w2s_packed), _stream(stream)))
 
 
-def lmoe_combine_norm_up(shape, y_perm, slot_of_pair, topk_w, gamma, w_up, y_shared, n_out, out, stream=None):
+def lmoe_combine_norm_up(shape, y_perm, slot_of_pair, topk_w, gamma, w_up, y_shared, n_out, out, h_shared=None,
+                         w2_shared=None, stream=None):
     out_dtype = LMOE_F32 if out.dtype == torch.float32 else LMOE_BF16
     _check("lmoe_combine_norm_up",
            lib().lmoe_combine_norm_up(ctypes.byref(shape), _ptr(y_perm), _ptr(slot_of_pair), _ptr(topk_w),
-                                      _ptr(gamma), _ptr(w_up), _ptr(y_shared), _ptr(n_out), _ptr(out), out_dtype,
-                                      _stream(stream)))
+                                      _ptr(gamma), _ptr(w_up), _ptr(y_shared), _ptr(h_shared), _ptr(w2_shared),
+                                      _ptr(n_out), _ptr(out), out_dtype, _stream(stream)))
 
 
 def profile_enable(on: bool) -> None:

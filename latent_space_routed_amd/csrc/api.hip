@@ -155,7 +155,7 @@ lmoe_status lmoe_permute(const lmoe_shape* sh, const void* x, const void* w_down
     return hip_status(launch_fill_i32(expert_offsets, sh->n_experts + 1, 0, static_cast<hipStream_t>(stream)));
   }
   if (!aligned16(x) || !aligned16(w_down) || !aligned4(topk_idx) || !aligned16(x_lat) || !aligned4(expert_offsets) ||
-      !aligned4(sorted_token) || !aligned4(slot_of_pair) || !aligned16(x_perm))
+      !aligned4(sorted_token) || !aligned4(slot_of_pair) || (x_perm && !aligned16(x_perm)))
     return LMOE_ERR_INVALID_ARGUMENT;
   const size_t need = permute_ws(sh);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return LMOE_ERR_WORKSPACE;
@@ -179,22 +179,26 @@ lmoe_status lmoe_permute(const lmoe_shape* sh, const void* x, const void* w_down
   st = hip_status(launch_permute(topk_idx, T, E, k, expert_offsets, sorted_token, slot_of_pair,
                                  static_cast<int32_t*>(workspace), s));
   if (st != LMOE_OK) return st;
+  if (!x_perm) return LMOE_OK;  // the routed GEMM gathers latent rows itself
   return hip_status(launch_gather_rows(x_lat, slot_of_pair, T, k, (int64_t)L * esize(sh->act_dtype), x_perm, s));
 }
 
 lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* sh, int32_t G, int32_t rows, int32_t K, int32_t inter,
-                                  int32_t n_out, const void* a_in, const int32_t* group_offsets, const void* w1,
-                                  const void* w2, void* h, void* y, int32_t y_dtype, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+                                  int32_t n_out, const void* a_in, int32_t a_rows, const int32_t* a_row_index,
+                                  const int32_t* group_offsets, const void* w1, const void* w2, void* h, void* y,
+                                  int32_t y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   lmoe_status st = check_shape(sh);
   if (st != LMOE_OK) return st;
-  if (G < 1 || rows < 0 || K <= 0 || inter <= 0 || n_out <= 0) return LMOE_ERR_INVALID_ARGUMENT;
-  if (y_dtype != LMOE_F32 && y_dtype != sh->act_dtype) return LMOE_ERR_INVALID_ARGUMENT;
+  if (G < 1 || rows < 0 || a_rows < 0 || K <= 0 || inter <= 0 || (w2 && n_out <= 0)) return LMOE_ERR_INVALID_ARGUMENT;
+  if (w2 && y_dtype != LMOE_F32 && y_dtype != sh->act_dtype) return LMOE_ERR_INVALID_ARGUMENT;
   if (K % 64 || inter % 64) return LMOE_ERR_UNSUPPORTED;
   if (!group_offsets && G != 1) return LMOE_ERR_INVALID_ARGUMENT;
+  if (!a_row_index && a_rows != rows) return LMOE_ERR_INVALID_ARGUMENT;
+  if (a_row_index && (int64_t)a_rows * K * esize(sh->act_dtype) > 0x7fff0000LL)
+    return LMOE_ERR_UNSUPPORTED;  // a gathered A is addressed with 31-bit byte offsets
   if (rows == 0) return LMOE_OK;
-  if (!aligned16(a_in) || !aligned16(w1) || !aligned16(w2) || !aligned16(h) || !aligned4(y) ||
-      (group_offsets && !aligned4(group_offsets)))
+  if (!aligned16(a_in) || !aligned16(w1) || !aligned16(h) || (a_row_index && !aligned4(a_row_index)) ||
+      (group_offsets && !aligned4(group_offsets)) || (w2 && (!aligned16(w2) || !aligned4(y))))
     return LMOE_ERR_INVALID_ARGUMENT;
   const size_t need = group_offsets ? glu_ws(G) : 0;
   if (need && (!workspace || workspace_bytes < need || !aligned16(workspace))) return LMOE_ERR_WORKSPACE;
@@ -215,6 +219,8 @@ lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* sh, int32_t G, int32_t rows,
   g1.A = a_in;
   g1.lda = K;
   g1.a_kwrap = K;
+  g1.a_rows = a_row_index;
+  g1.a_nrows = a_rows;
   g1.B = w1;
   g1.ldb = K;
   g1.b_gstride = (int64_t)2 * inter * K;
@@ -232,12 +238,14 @@ lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* sh, int32_t G, int32_t rows,
   g1.beta2 = sh->beta2;
   g1.tag = group_offsets ? "gemm_glu_grouped" : "gemm_glu_dense";
   st = hip_status(launch_gemm(g1, dt, Epi::Glu, shape, s));
-  if (st != LMOE_OK) return st;
+  if (st != LMOE_OK || !w2) return st;
 
   GemmArgs g2 = g1;
   g2.A = h;
   g2.lda = inter;
   g2.a_kwrap = inter;
+  g2.a_rows = nullptr;
+  g2.a_nrows = rows;
   g2.B = w2;
   g2.ldb = inter;
   g2.b_gstride = (int64_t)n_out * inter;
@@ -264,13 +272,18 @@ lmoe_status lmoe_pack_shared(const lmoe_shape* sh, const void* w1s, const void* 
 
 lmoe_status lmoe_combine_norm_up(const lmoe_shape* sh, const void* y_perm, const int32_t* slot_of_pair,
                                  const float* topk_w, const float* gamma, const void* w_up, const float* y_shared,
-                                 void* n_out, void* out, int32_t out_dtype, void* stream) {
+                                 const void* h_shared, const void* w2_shared, void* n_out, void* out,
+                                 int32_t out_dtype, void* stream) {
   lmoe_status st = check_shape(sh);
   if (st != LMOE_OK) return st;
   if (out_dtype != LMOE_F32 && out_dtype != sh->act_dtype) return LMOE_ERR_INVALID_ARGUMENT;
   if (sh->T == 0) return LMOE_OK;
+  if ((h_shared != nullptr) != (w2_shared != nullptr) || (h_shared && y_shared)) return LMOE_ERR_INVALID_ARGUMENT;
+  const int Ss = sh->n_shared * sh->inter_shared;
+  if (h_shared && Ss < 64) return LMOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(y_perm) || !aligned4(slot_of_pair) || !aligned4(topk_w) || (gamma && !aligned4(gamma)) ||
-      !aligned16(w_up) || (y_shared && !aligned4(y_shared)) || !aligned16(n_out) || !aligned16(out))
+      !aligned16(w_up) || (y_shared && !aligned4(y_shared)) || (h_shared && !aligned16(h_shared)) ||
+      (w2_shared && !aligned16(w2_shared)) || !aligned16(n_out) || !aligned16(out))
     return LMOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int T = sh->T, D = sh->d_model, L = sh->d_latent;
@@ -281,6 +294,7 @@ lmoe_status lmoe_combine_norm_up(const lmoe_shape* sh, const void* y_perm, const
   a.A = n_out;
   a.lda = L;
   a.a_kwrap = L;
+  a.a_nrows = T;
   a.B = w_up;
   a.ldb = L;
   a.C = out;
@@ -292,7 +306,16 @@ lmoe_status lmoe_combine_norm_up(const lmoe_shape* sh, const void* y_perm, const
   a.residual = y_shared;
   a.ldr = D;
   a.tag = "gemm_up";
-  return hip_status(launch_gemm(a, sh->act_dtype, y_shared ? Epi::AddF32 : Epi::Store, dense_shape(T, ceil_div(D, 256)), s));
+  if (h_shared) {  // out = [n | h_s] . [w_up | w2_shared]^T: one accumulator for both products
+    a.A2 = h_shared;
+    a.lda2 = Ss;
+    a.B2 = w2_shared;
+    a.ldb2 = Ss;
+    a.K1 = L;
+    a.K = L + Ss;
+  }
+  return hip_status(
+      launch_gemm(a, sh->act_dtype, y_shared ? Epi::AddF32 : Epi::Store, dense_shape(T, ceil_div(D, 256)), s));
 }
 
 }  // extern "C"

@@ -104,6 +104,15 @@ struct GemmArgs {
   const float* residual;       // AddF32: [M, N] f32
   int64_t ldr;
   const char* tag;             // kernel name for timing
+  // Row gather of A: GEMM row r reads A row a_rows[r] (a_nrows rows in A); nullptr = row r.
+  const int32_t* a_rows;
+  int a_nrows;
+  // Second K segment: k >= K1 reads A2 [M, K - K1] and B2 [N, K - K1] (nullptr = none, K1 = K).
+  const void* A2;
+  int64_t lda2;
+  const void* B2;
+  int64_t ldb2;
+  int K1;
 };
 
 enum class GemmShape : int { Big = 0, Small = 1 };

@@ -24,6 +24,10 @@
 //  * Global loads use buffer resources that span exactly the tile's valid rows of A and of B (one
 //    each for the gate and up halves of a GLU tile): past the end a load returns zero, so ragged
 //    row and column tails need no predication. The K offset rides in the uniform soffset.
+//  * Optional row gather of A (row r of the GEMM reads A row a_rows[r]): the routed experts read
+//    their tokens' latent rows in place, so the permuted copy is never written. Optional second K
+//    segment (A2, B2): the up-projection and the shared experts' down-projection share one
+//    output and one accumulator, [n | h_s] . [W_up | W2_s]^T.
 //  * The GLU epilogue needs gate column c and up column c in the same lane: a wave's first WN/2
 //    column-blocks read gate rows of B and its last WN/2 the matching up rows, so the MFMA result
 //    layouts coincide and SiTU-GLU is applied in registers (unfused it costs an extra pass over
@@ -68,6 +72,7 @@ struct Mfma<float> {
 // Raw buffer descriptor over [base, base + bytes): word 3 = 0x00020000 is the gfx9-family raw
 // buffer format (32-bit data, no swizzle); reads past num_records return zero.
 constexpr unsigned kBufWord3 = 0x00020000u;
+constexpr int kOutOfRange = 0x7fff0000;  // a voffset past any buffer this library builds: reads zero
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufWord3);
@@ -246,40 +251,66 @@ gemm_dma_kernel(GemmArgs p) {
   const int na = min(WM, max(0, (((t.rows + 31) >> 5) - wm + WAVES_M - 1) / WAVES_M));
 
   const int64_t a_ld = p.lda * (int64_t)sizeof(TI), b_ld = p.ldb * (int64_t)sizeof(TI);
+  const int64_t a_ld2 = p.lda2 * (int64_t)sizeof(TI), b_ld2 = p.ldb2 * (int64_t)sizeof(TI);
   const char* Bb = static_cast<const char*>(p.B) + (int64_t)t.g * p.b_gstride * (int64_t)sizeof(TI);
   const int ncols = min(BNO, p.N - t.n0);
-  const u32x4 a_desc = make_desc(static_cast<const char*>(p.A) + (int64_t)t.row0 * a_ld, (int)(t.rows * a_ld));
+  const bool gather = p.a_rows != nullptr;
+  const bool seg2 = !GLU && p.A2 != nullptr;
+  const u32x4 a_desc = gather ? make_desc(p.A, (int)(p.a_nrows * a_ld))
+                              : make_desc(static_cast<const char*>(p.A) + (int64_t)t.row0 * a_ld, (int)(t.rows * a_ld));
   const u32x4 b_desc0 = make_desc(Bb + (int64_t)t.n0 * b_ld, (int)(ncols * b_ld));
   const u32x4 b_desc1 = GLU ? make_desc(Bb + (int64_t)(p.glu_up_off + t.n0) * b_ld, (int)(ncols * b_ld)) : b_desc0;
+  const u32x4 a2_desc =
+      seg2 ? make_desc(static_cast<const char*>(p.A2) + (int64_t)t.row0 * a_ld2, (int)(t.rows * a_ld2)) : a_desc;
+  const u32x4 b2_desc =
+      seg2 ? make_desc(static_cast<const char*>(p.B2) + (int64_t)t.n0 * b_ld2, (int)(ncols * b_ld2)) : b_desc0;
   const int a_wrap = p.a_kwrap * (int)sizeof(TI);
   const int KT = p.K * (int)sizeof(TI) / KB;
+  const int KT1 = p.K1 * (int)sizeof(TI) / KB;
 
   // The lane's source chunk for each DMA block of this wave (swizzled so that LDS slot s of row r
-  // holds chunk s ^ ((r >> 1) & 3)).
+  // holds chunk s ^ ((r >> 1) & 3)). A gathered row outside A gets an offset past the buffer end.
   const int lr = lane >> 2, slot = lane & 3;
-  int a_voff[A_PW], b_voff[B_PW];
+  int a_voff[A_PW], b_voff[B_PW], a2_voff[A_PW], b2_voff[B_PW];
 #pragma unroll
   for (int i = 0; i < A_PW; ++i) {
     const int r = (wave * A_PW + i) * RPD + lr;
-    a_voff[i] = r * (int)a_ld + ((slot ^ ((r >> 1) & 3)) * 16);
+    const int ch = (slot ^ ((r >> 1) & 3)) * 16;
+    if (gather) {
+      const int src = r < t.rows ? p.a_rows[t.row0 + r] : -1;
+      a_voff[i] = (src >= 0 && src < p.a_nrows) ? src * (int)a_ld + ch : kOutOfRange;
+    } else {
+      a_voff[i] = r * (int)a_ld + ch;
+    }
+    a2_voff[i] = r * (int)a_ld2 + ch;
   }
 #pragma unroll
   for (int i = 0; i < B_PW; ++i) {
     const int r = (wave * B_PW + i) * RPD + lr;
-    b_voff[i] = (r % BNO) * (int)b_ld + ((slot ^ ((r >> 1) & 3)) * 16);
+    const int ch = (slot ^ ((r >> 1) & 3)) * 16;
+    b_voff[i] = (r % BNO) * (int)b_ld + ch;
+    b2_voff[i] = (r % BNO) * (int)b_ld2 + ch;
   }
   const unsigned lds0 = __builtin_amdgcn_readfirstlane(
       (unsigned)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
 
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
-    const int ka = (kt * KB) % a_wrap;
     const unsigned base = lds0 + stage * STAGE;
+    if (!seg2 || kt < KT1) {
+      const int ka = (kt * KB) % a_wrap;
 #pragma unroll
-    for (int i = 0; i < A_PW; ++i) dma16(a_desc, a_voff[i], ka, base + (wave * A_PW + i) * 1024);
+      for (int i = 0; i < A_PW; ++i) dma16(a_desc, a_voff[i], ka, base + (wave * A_PW + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < B_PW; ++i) {
-      const bool up = GLU && (wave * B_PW + i) * RPD >= BNO;
-      dma16(up ? b_desc1 : b_desc0, b_voff[i], kt * KB, base + A_BYTES + (wave * B_PW + i) * 1024);
+      for (int i = 0; i < B_PW; ++i) {
+        const bool up = GLU && (wave * B_PW + i) * RPD >= BNO;
+        dma16(up ? b_desc1 : b_desc0, b_voff[i], kt * KB, base + A_BYTES + (wave * B_PW + i) * 1024);
+      }
+    } else {
+      const int kk = (kt - KT1) * KB;
+#pragma unroll
+      for (int i = 0; i < A_PW; ++i) dma16(a2_desc, a2_voff[i], kk, base + (wave * A_PW + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < B_PW; ++i) dma16(b2_desc, b2_voff[i], kk, base + A_BYTES + (wave * B_PW + i) * 1024);
     }
   };
   constexpr int PER_TILE = A_PW + B_PW;  // DMA instructions per wave per K-tile
@@ -363,38 +394,62 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_reg_kernel(GemmA
   const int na = min(WM, max(0, (((t.rows + 31) >> 5) - wm + WAVES_M - 1) / WAVES_M));
 
   const int64_t a_ld = p.lda * (int64_t)sizeof(TI), b_ld = p.ldb * (int64_t)sizeof(TI);
+  const int64_t a_ld2 = p.lda2 * (int64_t)sizeof(TI), b_ld2 = p.ldb2 * (int64_t)sizeof(TI);
   const char* Bb = static_cast<const char*>(p.B) + (int64_t)t.g * p.b_gstride * (int64_t)sizeof(TI);
   const int ncols = min(BNO, p.N - t.n0);
+  const bool gather = p.a_rows != nullptr;
+  const bool seg2 = !GLU && p.A2 != nullptr;
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      make_rsrc(static_cast<const char*>(p.A) + (int64_t)t.row0 * a_ld, (int)(t.rows * a_ld));
+      gather ? make_rsrc(p.A, (int)(p.a_nrows * a_ld))
+             : make_rsrc(static_cast<const char*>(p.A) + (int64_t)t.row0 * a_ld, (int)(t.rows * a_ld));
   const __amdgpu_buffer_rsrc_t b_rsrc0 = make_rsrc(Bb + (int64_t)t.n0 * b_ld, (int)(ncols * b_ld));
   const __amdgpu_buffer_rsrc_t b_rsrc1 =
       GLU ? make_rsrc(Bb + (int64_t)(p.glu_up_off + t.n0) * b_ld, (int)(ncols * b_ld)) : b_rsrc0;
+  const __amdgpu_buffer_rsrc_t a2_rsrc =
+      seg2 ? make_rsrc(static_cast<const char*>(p.A2) + (int64_t)t.row0 * a_ld2, (int)(t.rows * a_ld2)) : a_rsrc;
+  const __amdgpu_buffer_rsrc_t b2_rsrc =
+      seg2 ? make_rsrc(static_cast<const char*>(p.B2) + (int64_t)t.n0 * b_ld2, (int)(ncols * b_ld2)) : b_rsrc0;
   const int a_wrap = p.a_kwrap * (int)sizeof(TI);
   const int KT = p.K * (int)sizeof(TI) / 128;
+  const int KT1 = p.K1 * (int)sizeof(TI) / 128;
 
-  int a_voff[A_PER], b_voff[B_PER];
+  int a_voff[A_PER], b_voff[B_PER], a2_voff[A_PER], b2_voff[B_PER];
 #pragma unroll
   for (int i = 0; i < A_PER; ++i) {
-    const int c = tid + i * NT;
-    a_voff[i] = (c >> 3) * (int)a_ld + (c & 7) * 16;
+    const int c = tid + i * NT, r = c >> 3;
+    if (gather) {
+      const int src = r < t.rows ? p.a_rows[t.row0 + r] : -1;
+      a_voff[i] = (src >= 0 && src < p.a_nrows) ? src * (int)a_ld + (c & 7) * 16 : kOutOfRange;
+    } else {
+      a_voff[i] = r * (int)a_ld + (c & 7) * 16;
+    }
+    a2_voff[i] = r * (int)a_ld2 + (c & 7) * 16;
   }
 #pragma unroll
   for (int i = 0; i < B_PER; ++i) {
     const int c = tid + i * NT;
     b_voff[i] = ((c >> 3) % BNO) * (int)b_ld + (c & 7) * 16;
+    b2_voff[i] = ((c >> 3) % BNO) * (int)b_ld2 + (c & 7) * 16;
   }
 
   uint4 ra[A_PER], rb[B_PER];
   int ka = 0;  // byte offset of the next K-tile inside A's (possibly wrapped) row
   auto gload = [&](int kt) __attribute__((always_inline)) {
+    if (!seg2 || kt < KT1) {
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) ra[i] = buffer_load16(a_rsrc, a_voff[i], ka);
+      for (int i = 0; i < A_PER; ++i) ra[i] = buffer_load16(a_rsrc, a_voff[i], ka);
 #pragma unroll
-    for (int i = 0; i < B_PER; ++i)
-      rb[i] = buffer_load16((GLU && (i * NT / 8) >= BNO) ? b_rsrc1 : b_rsrc0, b_voff[i], kt * 128);
-    ka += 128;
-    if (ka == a_wrap) ka = 0;
+      for (int i = 0; i < B_PER; ++i)
+        rb[i] = buffer_load16((GLU && (i * NT / 8) >= BNO) ? b_rsrc1 : b_rsrc0, b_voff[i], kt * 128);
+      ka += 128;
+      if (ka == a_wrap) ka = 0;
+    } else {
+      const int kk = (kt - KT1) * 128;
+#pragma unroll
+      for (int i = 0; i < A_PER; ++i) ra[i] = buffer_load16(a2_rsrc, a2_voff[i], kk);
+#pragma unroll
+      for (int i = 0; i < B_PER; ++i) rb[i] = buffer_load16(b2_rsrc, b2_voff[i], kk);
+    }
   };
   auto lstore = [&](int stage) __attribute__((always_inline)) {
     char* base = smem + stage * STAGE;

@@ -6,6 +6,10 @@ FFNs, combine, norm, up-project, shared experts added):
   -> lmoe_grouped_situ_glu (shared experts, one group) -> lmoe_combine_norm_up
 and, at a step boundary, lmoe_qb_update. Every step runs in the library's kernels; this module only
 allocates buffers and passes pointers.
+
+fused=True (default): the routed GEMM reads x_lat rows through sorted_token (no permuted copy), and
+the shared experts' down-projection is folded into the up-projection's accumulation (no y_sh).
+fused=False materialises x_perm and y_sh, as separate steps.
 """
 from __future__ import annotations
 
@@ -31,9 +35,10 @@ class LatentMoE:
     """One layer instance: weights on the device, per-batch buffers sized for up to ``max_tokens``."""
 
     def __init__(self, cfg, weights: dict, max_tokens: int | None = None, device: str = "cuda",
-                 out_dtype: torch.dtype = torch.float32):
+                 out_dtype: torch.dtype = torch.float32, fused: bool = True):
         self.cfg = cfg
         self.out_dtype = out_dtype
+        self.fused = fused
         self.device = device
         self.max_tokens = cfg.T if max_tokens is None else max_tokens
         self.w = weights
@@ -67,11 +72,11 @@ class LatentMoE:
             "offsets": torch.empty(E + 1, dtype=i32, device=dev),
             "sorted_token": torch.empty(T * k, dtype=i32, device=dev),
             "slot_of_pair": torch.empty(T * k, dtype=i32, device=dev),
-            "x_perm": torch.empty(T * k, L, dtype=dt, device=dev),
+            "x_perm": torch.empty(0 if self.fused else T * k, L, dtype=dt, device=dev),
             "h": torch.empty(T * k, I, dtype=dt, device=dev),
             "y": torch.empty(T * k, L, dtype=dt, device=dev),
             "h_s": torch.empty(T, max(S * Is, 64), dtype=dt, device=dev),
-            "y_sh": torch.empty(T, D, dtype=f32, device=dev),
+            "y_sh": torch.empty(0 if self.fused else T, D, dtype=f32, device=dev),
             "n": torch.empty(T, L, dtype=dt, device=dev),
             "out": torch.empty(T, D, dtype=self.out_dtype, device=dev),
         }
@@ -89,12 +94,14 @@ class LatentMoE:
         if T > self.max_tokens:
             self.max_tokens = T
             self._alloc(T)
-        b = {k: (v[:T] if k in ("scores", "idx", "w", "thresh", "x_lat", "h_s", "y_sh", "n", "out") else v)
+        b = {k: (v[:T] if k in ("scores", "idx", "w", "thresh", "x_lat", "h_s", "n", "out") else v)
              for k, v in self._bufs.items()}
+        b["y_sh"] = self._bufs["y_sh"][:T] if not self.fused else None
         for k in ("sorted_token", "slot_of_pair"):
             b[k] = self._bufs[k][: T * cfg.top_k]
-        for k in ("x_perm", "h", "y"):
+        for k in ("h", "y"):
             b[k] = self._bufs[k][: T * cfg.top_k]
+        b["x_perm"] = self._bufs["x_perm"][: T * cfg.top_k] if not self.fused else None
         shape = C.make_shape(cfg, T)
         E, k, L, D, I = cfg.n_experts, cfg.top_k, cfg.d_latent, cfg.d_model, cfg.inter
         S, Is = cfg.n_shared, cfg.inter_shared
@@ -103,17 +110,28 @@ class LatentMoE:
         if accumulate_hist:
             C.lmoe_qb_histogram(shape, b["scores"], self.bias, b["idx"], b["thresh"], self.hist)
             self.n_acc += T
+        fused = self.fused
         C.lmoe_permute(shape, x, w["w_down"], b["idx"], b["x_lat"], b["offsets"], b["sorted_token"],
-                       b["slot_of_pair"], b["x_perm"], b["ws_permute"])
-        C.lmoe_grouped_situ_glu(shape, E, T * k, L, I, L, b["x_perm"], b["offsets"], w["w1"], w["w2"], b["h"],
-                                b["y"], b["ws_glu"])
-        y_sh = None
-        if S > 0:
+                       b["slot_of_pair"], None if fused else b["x_perm"], b["ws_permute"])
+        if fused:
+            C.lmoe_grouped_situ_glu(shape, E, T * k, L, I, L, b["x_lat"], b["offsets"], w["w1"], w["w2"], b["h"],
+                                    b["y"], b["ws_glu"], a_row_index=b["sorted_token"])
+        else:
+            C.lmoe_grouped_situ_glu(shape, E, T * k, L, I, L, b["x_perm"], b["offsets"], w["w1"], w["w2"], b["h"],
+                                    b["y"], b["ws_glu"])
+        if S > 0 and fused:
+            C.lmoe_grouped_situ_glu(shape, 1, T, D, S * Is, D, x, None, self.w1s_packed, None, b["h_s"], None,
+                                    b["ws_glu"])
+            C.lmoe_combine_norm_up(shape, b["y"], b["slot_of_pair"], b["w"], w.get("gamma"), w["w_up"], None,
+                                   b["n"], b["out"], h_shared=b["h_s"], w2_shared=self.w2s_packed)
+        elif S > 0:
             C.lmoe_grouped_situ_glu(shape, 1, T, D, S * Is, D, x, None, self.w1s_packed, self.w2s_packed,
                                     b["h_s"], b["y_sh"], b["ws_glu"])
-            y_sh = b["y_sh"]
-        C.lmoe_combine_norm_up(shape, b["y"], b["slot_of_pair"], b["w"], w.get("gamma"), w["w_up"], y_sh, b["n"],
-                               b["out"])
+            C.lmoe_combine_norm_up(shape, b["y"], b["slot_of_pair"], b["w"], w.get("gamma"), w["w_up"], b["y_sh"],
+                                   b["n"], b["out"])
+        else:
+            C.lmoe_combine_norm_up(shape, b["y"], b["slot_of_pair"], b["w"], w.get("gamma"), w["w_up"], None,
+                                   b["n"], b["out"])
         return b
 
     def qb_update(self) -> None:

@@ -33,9 +33,9 @@ def cached_inputs(cfg, seed: int = 0, batch: int = 0):
     return make_inputs(cfg, seed=seed, batch=batch)
 
 
-def device_layer(cfg, inp: dict, max_tokens=None) -> tuple[LatentMoE, torch.Tensor]:
+def device_layer(cfg, inp: dict, max_tokens=None, fused: bool = True) -> tuple[LatentMoE, torch.Tensor]:
     w = upload_weights(inp, cfg.act_dtype)
-    layer = LatentMoE(cfg, w, max_tokens=max_tokens)
+    layer = LatentMoE(cfg, w, max_tokens=max_tokens, fused=fused)
     x = to_device(inp["x"], cfg.act_dtype)
     return layer, x
 

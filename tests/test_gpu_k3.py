@@ -61,7 +61,7 @@ def check_sampled_tokens(cfg, inp, b, tokens, what):
     y = host(b["y"][sl]).reshape(len(tokens), k, -1)
     n = host(b["n"][tok])
     h_s = host(b["h_s"][tok])[:, : cfg.n_shared * cfg.inter_shared]
-    y_sh = host(b["y_sh"][tok])
+    y_sh = host(b["y_sh"][tok]) if b["y_sh"] is not None else None
     out = host(b["out"][tok])
     x = O.to_f64(np.asarray(inp["x"])[tokens], dt)
     assert_close_rows(x_lat, O.down_project(x, O.to_f64(inp["w_down"], dt), dt), dt, f"{what} x_lat")
@@ -80,8 +80,11 @@ def check_sampled_tokens(cfg, inp, b, tokens, what):
     h_s_ref, _ = O.shared_experts(x, O.to_f64(inp["w1s"], dt), O.to_f64(inp["w2s"], dt), cfg.beta1, cfg.beta2, dt)
     assert_close_rows(h_s, h_s_ref, dt, f"{what} h_s")
     w2s_cat = np.concatenate(list(O.to_f64(inp["w2s"], dt)), axis=1)
-    assert_close_rows(y_sh, O.store(h_s @ w2s_cat.T, "f32"), "f32", f"{what} y_sh")
-    pre, _ = O.up_project(n, O.to_f64(inp["w_up"], dt), y_sh, dt)
+    if y_sh is not None:  # materialised shared output
+        assert_close_rows(y_sh, O.store(h_s @ w2s_cat.T, "f32"), "f32", f"{what} y_sh")
+        pre, _ = O.up_project(n, O.to_f64(inp["w_up"], dt), y_sh, dt)
+    else:  # shared down-projection accumulated with the up-projection
+        pre, _ = O.up_project(n, O.to_f64(inp["w_up"], dt), h_s @ w2s_cat.T, dt)
     assert_close_rows(out, pre, "f32", f"{what} out from the GPU's n")
     ex = O.expert_path(inp, cfg, g_idx, g_w, tokens=tokens)
     return assert_out_parity(out, ex["out_pre"], dt, f"{what} out end to end (GPU routing, {len(tokens)} tokens)")
@@ -98,8 +101,9 @@ def check_routing_all_tokens(cfg, inp, x_host, b, bias):
     np.testing.assert_array_equal(host(b["offsets"]), off)
     np.testing.assert_array_equal(host(b["sorted_token"]), st)
     np.testing.assert_array_equal(host(b["slot_of_pair"]), sp)
-    st_dev = torch.as_tensor(st, device="cuda", dtype=torch.long)
-    assert torch.equal(b["x_perm"].view(torch.int16), b["x_lat"][st_dev].view(torch.int16))
+    if b["x_perm"] is not None:
+        st_dev = torch.as_tensor(st, device="cuda", dtype=torch.long)
+        assert torch.equal(b["x_perm"].view(torch.int16), b["x_lat"][st_dev].view(torch.int16))
     return s, idx, thr
 
 

@@ -25,20 +25,31 @@ pytestmark = pytest.mark.gpu
 TINY = CONFIGS["tiny_f32"]
 MID = CONFIGS["mid_bf16"]
 SMALL_CASES = [TINY, replace(TINY, name="tiny_ragged", T=77), MID, replace(MID, name="mid_ragged", T=1000)]
-IDS = [c.name for c in SMALL_CASES]
+# fused: routed GEMM gathers x_lat rows, shared down-projection folded into the up-projection;
+# unfused: x_perm and y_sh materialised
+RUNS = [(c, f) for c in SMALL_CASES for f in (True, False)]
+IDS = [f"{c.name}-{'fused' if f else 'unfused'}" for c, f in RUNS]
+_ORACLE = {}
 
 
-@pytest.fixture(scope="module", params=SMALL_CASES, ids=IDS)
+def oracle_forward(cfg, inp):
+    if cfg.name not in _ORACLE:
+        _ORACLE[cfg.name] = O.forward(inp, cfg)
+    return _ORACLE[cfg.name]
+
+
+@pytest.fixture(scope="module", params=RUNS, ids=IDS)
 def run(request):
-    cfg = request.param
-    say(f"[case] {cfg.name} T={cfg.T}")
+    cfg, fused = request.param
+    say(f"[case] {cfg.name} T={cfg.T} fused={fused}")
     inp = cached_inputs(cfg)
-    layer, x = device_layer(cfg, inp)
+    layer, x = device_layer(cfg, inp, fused=fused)
     b = layer.forward(x)
     torch.cuda.synchronize()
-    g = {k: host(v) for k, v in b.items() if not k.startswith("ws_")}
+    g = {k: host(v) for k, v in b.items() if not k.startswith("ws_") and v is not None}
     g["hist"] = layer.hist.cpu().numpy().view(np.uint32).copy()
-    ref = O.forward(inp, cfg)
+    g["fused"] = fused
+    ref = oracle_forward(cfg, inp)
     return cfg, inp, layer, x, g, ref
 
 
@@ -108,7 +119,8 @@ def test_permute_bit_exact(run):
     np.testing.assert_array_equal(g["offsets"], off)
     np.testing.assert_array_equal(g["sorted_token"], st)
     np.testing.assert_array_equal(g["slot_of_pair"], sp)
-    np.testing.assert_array_equal(g["x_perm"], g["x_lat"][g["sorted_token"]])
+    if not g["fused"]:
+        np.testing.assert_array_equal(g["x_perm"], g["x_lat"][g["sorted_token"]])
     e = assert_close_rows(g["x_lat"], ref["x_lat"], cfg.act_dtype, "x_lat")
     say(f"{cfg.name}: x_lat max err/RMS {e:.2e}")
 
@@ -119,10 +131,11 @@ def test_grouped_glu_parity(run):
     h_ref = np.zeros_like(g["h"])
     y_ref = np.zeros_like(g["y"])
     off = g["offsets"]
+    rows_in = g["x_lat"][g["sorted_token"]]  # the GEMM's A rows, gathered or materialised
     for e in range(cfg.n_experts):
         r0, r1 = off[e], off[e + 1]
         if r1 > r0:
-            h_ref[r0:r1], y_ref[r0:r1] = O.situ_glu_ffn(g["x_perm"][r0:r1], O.to_f64(inp["w1"][e], dt),
+            h_ref[r0:r1], y_ref[r0:r1] = O.situ_glu_ffn(rows_in[r0:r1], O.to_f64(inp["w1"][e], dt),
                                                         O.to_f64(inp["w2"][e], dt), cfg.beta1, cfg.beta2, dt)
     assert_close_rows(g["h"], h_ref, dt, "h")
     # y from the GPU's own h isolates GEMM2 from the h rounding of GEMM1
@@ -139,8 +152,9 @@ def test_shared_experts_parity(run):
     dt = cfg.act_dtype
     S, Is = cfg.n_shared, cfg.inter_shared
     assert_close_rows(g["h_s"][:, : S * Is], ref["h_s"], dt, "h_s")
-    ysh = O.store(g["h_s"][:, : S * Is] @ np.concatenate(list(O.to_f64(inp["w2s"], dt)), axis=1).T, "f32")
-    assert_close_rows(g["y_sh"], ysh, "f32" if dt == "f32" else "bf16", "y_sh")
+    if not g["fused"]:
+        ysh = O.store(g["h_s"][:, : S * Is] @ np.concatenate(list(O.to_f64(inp["w2s"], dt)), axis=1).T, "f32")
+        assert_close_rows(g["y_sh"], ysh, "f32" if dt == "f32" else "bf16", "y_sh")
 
 
 def test_combine_norm_up_parity(run):
@@ -151,7 +165,12 @@ def test_combine_norm_up_parity(run):
     z = O.combine(y_pairs, g["w"].astype(np.float32))
     n_ref = O.store(O.rms_norm(z, inp["gamma"], cfg.rms_eps), dt)
     assert_close_rows(g["n"], n_ref, dt, "n")
-    pre, _ = O.up_project(g["n"], O.to_f64(inp["w_up"], dt), g["y_sh"], dt)
+    if g["fused"]:
+        S, Is = cfg.n_shared, cfg.inter_shared
+        w2s_cat = np.concatenate(list(O.to_f64(inp["w2s"], dt)), axis=1)
+        pre, _ = O.up_project(g["n"], O.to_f64(inp["w_up"], dt), g["h_s"][:, : S * Is] @ w2s_cat.T, dt)
+    else:
+        pre, _ = O.up_project(g["n"], O.to_f64(inp["w_up"], dt), g["y_sh"], dt)
     assert_close_rows(g["out"], pre, "f32", "out (from the GPU's n)")
 
 
@@ -172,7 +191,8 @@ def test_deterministic(run):
     b = layer.forward(x, accumulate_hist=False)
     torch.cuda.synchronize()
     for name in ("scores", "idx", "w", "thresh", "x_lat", "offsets", "slot_of_pair", "x_perm", "h", "y", "n", "out"):
-        np.testing.assert_array_equal(host(b[name]), g[name], err_msg=name)
+        if b[name] is not None:
+            np.testing.assert_array_equal(host(b[name]), g[name], err_msg=name)
 
 
 # ---------------------------------------------------------------------------------------------------
