@@ -41,7 +41,8 @@ def source_digest() -> str:
 
 def glu_bytes(cfg, offsets) -> tuple[float, float]:
     """Algorithmic HBM bytes and FLOPs of one routed GEMM1 launch: the W1 slices of the experts that
-    received tokens, the permuted latent rows read once, and h written once."""
+    received tokens, each token's latent row read once (the GEMM gathers rows of x_lat in place),
+    and h written once."""
     import numpy as np
 
     counts = np.diff(offsets)
@@ -49,7 +50,7 @@ def glu_bytes(cfg, offsets) -> tuple[float, float]:
     rows = int(offsets[-1])
     esz = 2 if cfg.act_dtype == "bf16" else 4
     w_bytes = touched * 2 * cfg.inter * cfg.d_latent * esz
-    a_bytes = rows * cfg.d_latent * esz
+    a_bytes = cfg.T * cfg.d_latent * esz
     h_bytes = rows * cfg.inter * esz
     flops = 2.0 * rows * cfg.d_latent * 2 * cfg.inter
     return float(w_bytes + a_bytes + h_bytes), flops

@@ -1,0 +1,100 @@
+"""The C-ABI library loads and exports every symbol include/lmoe.h declares; host-side argument
+validation answers before any GPU work (no compute calls here, so this runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from latent_space_routed_amd import _lib as C
+from workloads import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lmoe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(C.LIB_PATH):
+        from latent_space_routed_amd import build
+        build.build()
+    return C.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lmoe_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(C.EXPORTS) == names
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["LMOE_OK", "LMOE_ERR_INVALID_ARGUMENT", "LMOE_ERR_UNSUPPORTED",
+                                 "LMOE_ERR_WORKSPACE", "LMOE_ERR_HIP"]):
+        assert C.status_string(code) == name
+
+
+def test_workspace_sizes(lib):
+    k3 = C.make_shape(CONFIGS["k3_prefill"])
+    assert C.workspace_bytes(k3, C.LMOE_CALL_ROUTE) == 3 * 896 * 7168 * 2          # bf16 split of W_r
+    assert C.workspace_bytes(k3, C.LMOE_CALL_PERMUTE) == 32 * 896 * 4             # per-chunk counts
+    assert C.workspace_bytes(k3, C.LMOE_CALL_GROUPED_GLU) == 3840                # tile prefix, rounded
+    assert C.workspace_bytes(C.make_shape(CONFIGS["tiny_f32"]), C.LMOE_CALL_ROUTE) == 0
+    bad = C.make_shape(CONFIGS["k3_prefill"])
+    bad.top_k = bad.n_experts
+    assert C.workspace_bytes(bad, C.LMOE_CALL_ROUTE) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("top_k", 896, C.LMOE_ERR_INVALID_ARGUMENT),     # (k+1)-th score must exist
+    ("top_k", 0, C.LMOE_ERR_INVALID_ARGUMENT),
+    ("T", -1, C.LMOE_ERR_INVALID_ARGUMENT),
+    ("act_dtype", 7, C.LMOE_ERR_INVALID_ARGUMENT),
+    ("d_latent", 3583, C.LMOE_ERR_UNSUPPORTED),      # not a multiple of 64
+    ("n_bins", 1, C.LMOE_ERR_UNSUPPORTED),
+    ("n_experts", 4096, C.LMOE_ERR_UNSUPPORTED),
+])
+def test_shape_validation_before_any_launch(lib, field, value, status):
+    sh = C.make_shape(CONFIGS["k3_prefill"])
+    setattr(sh, field, value)
+    null = None
+    assert lib.lmoe_route(ctypes.byref(sh), null, null, null, null, null, null, null, null, null, 0, null) == status
+    assert lib.lmoe_qb_histogram(ctypes.byref(sh), null, null, null, null, null, null) == status
+    assert lib.lmoe_qb_update(ctypes.byref(sh), null, 1, null, null) == status
+
+
+def test_pointer_validation_before_any_launch(lib):
+    sh = C.make_shape(CONFIGS["k3_prefill"])
+    null = None
+    fake = ctypes.c_void_p(0x1000)        # aligned, never dereferenced: validation fails first
+    misaligned = ctypes.c_void_p(0x1002)
+    assert lib.lmoe_qb_update(ctypes.byref(sh), null, 1, fake, null) == C.LMOE_ERR_INVALID_ARGUMENT
+    assert lib.lmoe_qb_histogram(ctypes.byref(sh), misaligned, fake, fake, fake, fake, null) == \
+        C.LMOE_ERR_INVALID_ARGUMENT
+    # route with every pointer plausible but no workspace -> workspace error, still no launch
+    assert lib.lmoe_route(ctypes.byref(sh), fake, fake, fake, null, fake, fake, fake, fake, null, 0, null) == \
+        C.LMOE_ERR_WORKSPACE
+    # grouped GLU: a row gather needs a_rows consistent; K not a multiple of 64 is unsupported
+    assert lib.lmoe_grouped_situ_glu(ctypes.byref(sh), 1, 16, 100, 64, 64, fake, 16, null, null, fake, fake, fake,
+                                     fake, 0, null, 0, null) == C.LMOE_ERR_UNSUPPORTED
+    assert lib.lmoe_grouped_situ_glu(ctypes.byref(sh), 1, 16, 128, 64, 64, fake, 8, null, null, fake, fake, fake,
+                                     fake, 0, null, 0, null) == C.LMOE_ERR_INVALID_ARGUMENT
+    # combine: y_shared and the folded shared pair are exclusive
+    assert lib.lmoe_combine_norm_up(ctypes.byref(sh), fake, fake, fake, null, fake, fake, fake, fake, fake, fake, 0,
+                                    null) == C.LMOE_ERR_INVALID_ARGUMENT
+
+
+def test_empty_batch_is_a_no_op(lib):
+    sh = C.make_shape(CONFIGS["k3_prefill"], T=0)
+    null = None
+    assert lib.lmoe_route(ctypes.byref(sh), null, null, null, null, null, null, null, null, null, 0, null) == C.LMOE_OK
+    assert lib.lmoe_qb_histogram(ctypes.byref(sh), null, null, null, null, null, null) == C.LMOE_OK
+    assert lib.lmoe_combine_norm_up(ctypes.byref(sh), null, null, null, null, null, null, null, null, null, null, 0,
+                                    null) == C.LMOE_OK
