@@ -198,7 +198,7 @@ lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* sh, int32_t G, int32_t rows,
     return LMOE_ERR_UNSUPPORTED;  // a gathered A is addressed with 31-bit byte offsets
   if (rows == 0) return LMOE_OK;
   if (!aligned16(a_in) || !aligned16(w1) || !aligned16(h) || (a_row_index && !aligned4(a_row_index)) ||
-      (group_offsets && !aligned4(group_offsets)) || (w2 && (!aligned16(w2) || !aligned4(y))))
+      (group_offsets && !aligned4(group_offsets)) || (w2 && (!aligned16(w2) || !aligned16(y))))
     return LMOE_ERR_INVALID_ARGUMENT;
   const size_t need = group_offsets ? glu_ws(G) : 0;
   if (need && (!workspace || workspace_bytes < need || !aligned16(workspace))) return LMOE_ERR_WORKSPACE;

@@ -15,8 +15,9 @@
 //      LDS with buffer_load ... lds, four LDS stages deep, so three K-tiles (96 KB per CU) are in
 //      flight while the MFMAs consume the fourth, without any register staging. A DMA instruction
 //      writes 64 lanes x 16 bytes contiguously (16 rows of 64 bytes); each lane fetches the chunk
-//      that belongs at its slot under an XOR swizzle (slot = chunk ^ ((row >> 1) & 3)), which makes
-//      the ds_read_b128 fragment reads of eight consecutive rows hit eight distinct bank groups.
+//      that belongs at its slot under an XOR swizzle (slot = chunk ^ ((row >> 2) & 3)). A
+//      ds_read_b128 is served 16 lanes (256 bytes of banks) at a time; the swizzle places the 16
+//      rows one pass reads in 16 distinct 16-byte bank groups.
 //      The DMA is issued from inline assembly with its own vmcnt waits, because the compiler's
 //      waitcnt pass would otherwise drain every outstanding DMA before each LDS read.
 //    - Registers (128x128 tiles): K-tiles of 128 bytes per row are loaded into registers one
@@ -100,6 +101,9 @@ __device__ inline void dma16(const u32x4& desc, int voff, int soff, unsigned lds
                : "s"(lds_addr), "v"(voff), "s"(desc), "s"(soff)
                : "memory", "m0");
 }
+
+// XOR key of the DMA pipeline's LDS layout: 16-byte slot of chunk c in row r is c ^ swz(r).
+__device__ constexpr int swz(int r) { return (r >> 2) & 3; }
 
 template <int N>
 __device__ inline void wait_vmcnt() {
@@ -196,6 +200,60 @@ __device__ inline void epilogue(const GemmArgs& p, const TileInfo& t, f32x16 (&a
   }
 }
 
+// Epilogue through LDS for Store/Glu into TO (bf16 or f32): the wave writes its outputs into its own
+// LDS region in row-major order, then every lane stores whole 16-byte chunks (one instruction per
+// 8 bf16 or 4 f32) instead of one scalar per element. Needs N and ldc multiples of 16 / sizeof(TO)
+// and a 16-byte aligned C. Row-blocks are staged RBP at a time to fit the region.
+template <typename TI, typename TO, int WAVES_M, int WAVES_N, int WM, int WN, Epi EPI, int REGION>
+__device__ inline void epilogue_staged(const GemmArgs& p, const TileInfo& t, f32x16 (&acc)[WM][WN], int wm, int wn,
+                                       int lane, int na, char* region) {
+  constexpr bool GLU = EPI == Epi::Glu;
+  static_assert(EPI == Epi::Store || GLU, "staged epilogue covers plain and GLU stores");
+  constexpr int WNO = GLU ? WN / 2 : WN;
+  constexpr int COLS = WNO * 32;
+  constexpr int ROWB = COLS * (int)sizeof(TO);
+  constexpr int VEC = 16 / (int)sizeof(TO);
+  constexpr int CPB = 32 / VEC;   // chunks per row of one 32-column block
+  constexpr int CPR = WNO * CPB;  // chunks per staged row
+  constexpr int RBP = REGION / (32 * ROWB) < WM ? REGION / (32 * ROWB) : WM;
+  static_assert(RBP >= 1, "region holds at least one row-block");
+  const float inv_b1 = 1.0f / p.beta1, inv_b2 = 1.0f / p.beta2;
+  TO* st = reinterpret_cast<TO*>(region);
+#pragma unroll
+  for (int i0 = 0; i0 < WM; i0 += RBP) {
+    if (i0 >= na) break;
+#pragma unroll
+    for (int ii = 0; ii < RBP; ++ii) {
+      const int i = i0 + ii;
+      if (i >= WM || i >= na) break;
+#pragma unroll
+      for (int j = 0; j < WNO; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int lr = ii * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+          float v = acc[i][j][q];
+          if constexpr (GLU) v = situ_glu<sizeof(TI) == 4>(v, acc[i][j + WNO][q], p.beta1, inv_b1, p.beta2, inv_b2);
+          if constexpr (sizeof(TO) == 2)
+            st[lr * COLS + j * 32 + (lane & 31)] = f32_to_bf16(v);
+          else
+            st[lr * COLS + j * 32 + (lane & 31)] = v;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int nrb = min(RBP, na - i0);
+    for (int c = lane; c < nrb * 32 * CPR; c += kWave) {
+      const int lr = c / CPR, cc = c % CPR;
+      const int j = cc / CPB, cv = (cc % CPB) * VEC;
+      const int r = ((i0 + lr / 32) * WAVES_M + wm) * 32 + (lr % 32);
+      const int col = t.n0 + (j * WAVES_N + wn) * 32 + cv;
+      if (r < t.rows && col < p.N)
+        *reinterpret_cast<uint4*>(static_cast<TO*>(p.C) + (int64_t)(t.row0 + r) * p.ldc + col) =
+            *reinterpret_cast<const uint4*>(region + lr * ROWB + (j * 32 + cv) * (int)sizeof(TO));
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 template <int WM, int WN>
 __device__ inline void zero_acc(f32x16 (&acc)[WM][WN]) {
 #pragma unroll
@@ -269,13 +327,13 @@ gemm_dma_kernel(GemmArgs p) {
   const int KT1 = p.K1 * (int)sizeof(TI) / KB;
 
   // The lane's source chunk for each DMA block of this wave (swizzled so that LDS slot s of row r
-  // holds chunk s ^ ((r >> 1) & 3)). A gathered row outside A gets an offset past the buffer end.
+  // holds chunk s ^ swz(r)). A gathered row outside A gets an offset past the buffer end.
   const int lr = lane >> 2, slot = lane & 3;
   int a_voff[A_PW], b_voff[B_PW], a2_voff[A_PW], b2_voff[B_PW];
 #pragma unroll
   for (int i = 0; i < A_PW; ++i) {
     const int r = (wave * A_PW + i) * RPD + lr;
-    const int ch = (slot ^ ((r >> 1) & 3)) * 16;
+    const int ch = (slot ^ swz(r)) * 16;
     if (gather) {
       const int src = r < t.rows ? p.a_rows[t.row0 + r] : -1;
       a_voff[i] = (src >= 0 && src < p.a_nrows) ? src * (int)a_ld + ch : kOutOfRange;
@@ -287,17 +345,17 @@ gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < B_PW; ++i) {
     const int r = (wave * B_PW + i) * RPD + lr;
-    const int ch = (slot ^ ((r >> 1) & 3)) * 16;
+    const int ch = (slot ^ swz(r)) * 16;
     b_voff[i] = (r % BNO) * (int)b_ld + ch;
     b2_voff[i] = (r % BNO) * (int)b_ld2 + ch;
   }
   const unsigned lds0 = __builtin_amdgcn_readfirstlane(
       (unsigned)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
 
+  int ka = 0;  // byte offset of the next issued K-tile inside A's (possibly wrapped) row
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
     const unsigned base = lds0 + stage * STAGE;
     if (!seg2 || kt < KT1) {
-      const int ka = (kt * KB) % a_wrap;
 #pragma unroll
       for (int i = 0; i < A_PW; ++i) dma16(a_desc, a_voff[i], ka, base + (wave * A_PW + i) * 1024);
 #pragma unroll
@@ -305,6 +363,8 @@ gemm_dma_kernel(GemmArgs p) {
         const bool up = GLU && (wave * B_PW + i) * RPD >= BNO;
         dma16(up ? b_desc1 : b_desc0, b_voff[i], kt * KB, base + A_BYTES + (wave * B_PW + i) * 1024);
       }
+      ka += KB;
+      if (ka == a_wrap) ka = 0;
     } else {
       const int kk = (kt - KT1) * KB;
 #pragma unroll
@@ -324,7 +384,7 @@ gemm_dma_kernel(GemmArgs p) {
   f32x16 acc[WM][WN];
   zero_acc(acc);
   // fragment offsets for the two 32-byte k-steps of a K-tile (row-block base added per block)
-  const int sw = ((lane & 31) >> 1) & 3;
+  const int sw = swz(lane & 31);  // row-block bases are multiples of 32, so only lane & 31 matters
   const int fo0 = (lane & 31) * KB + (((lane >> 5) ^ sw) * 16);
   const int fo1 = (lane & 31) * KB + (((2 + (lane >> 5)) ^ sw) * 16);
 
@@ -360,6 +420,20 @@ gemm_dma_kernel(GemmArgs p) {
       if (NA > 0) compute(kt % NS);
     }
   });
+  if constexpr (EPI == Epi::Store || EPI == Epi::Glu) {
+    constexpr int REGION = NS * STAGE / NW;  // each wave's slice of the pipeline LDS
+    const bool bf = p.c_dtype == LMOE_BF16;
+    const int vec = bf ? 8 : 4;
+    if (p.N % vec == 0 && p.ldc % vec == 0) {
+      __syncthreads();  // every wave is done reading the pipeline stages
+      char* region = smem + wave * REGION;
+      if (bf)
+        epilogue_staged<TI, uint16_t, WAVES_M, WAVES_N, WM, WN, EPI, REGION>(p, t, acc, wm, wn, lane, na, region);
+      else
+        epilogue_staged<TI, float, WAVES_M, WAVES_N, WM, WN, EPI, REGION>(p, t, acc, wm, wn, lane, na, region);
+      return;
+    }
+  }
   epilogue<TI, WAVES_M, WAVES_N, WM, WN, EPI>(p, t, acc, wm, wn, lane, na);
 }
 
