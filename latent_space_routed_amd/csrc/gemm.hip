@@ -11,13 +11,14 @@
 //    rows of the tile form a prefix, and the K loop is instantiated per prefix length, so no
 //    branch sits between the LDS reads and the MFMAs and empty row-blocks cost nothing.
 //  * Two pipelines:
-//    - DMA (256x256 tiles): K-tiles of 32 bf16 (64 bytes of each row) go straight from HBM into
-//      LDS with buffer_load ... lds, four LDS stages deep, so three K-tiles (96 KB per CU) are in
-//      flight while the MFMAs consume the fourth, without any register staging. A DMA instruction
-//      writes 64 lanes x 16 bytes contiguously (16 rows of 64 bytes); each lane fetches the chunk
-//      that belongs at its slot under an XOR swizzle (slot = chunk ^ ((row >> 2) & 3)). A
-//      ds_read_b128 is served 16 lanes (256 bytes of banks) at a time; the swizzle places the 16
-//      rows one pass reads in 16 distinct 16-byte bank groups.
+//    - DMA (256x256 tiles): K-tiles go straight from HBM into LDS with buffer_load ... lds, without
+//      register staging, into a ring of NS stages (measured best: two stages of 64 bf16 per row,
+//      64 KB each; the next K-tile streams in while the MFMAs consume the current one, and the
+//      wider K-tile halves the barriers against four stages of 32). A DMA instruction writes 64
+//      lanes x 16 bytes contiguously (1 KB of consecutive rows); each lane fetches the chunk that
+//      belongs at its slot under an XOR swizzle. A ds_read_b128 is served 16 lanes (256 bytes of
+//      banks) at a time, and the swizzle places the 16 rows one pass reads in 16 distinct 16-byte
+//      bank groups.
 //      The DMA is issued from inline assembly with its own vmcnt waits, because the compiler's
 //      waitcnt pass would otherwise drain every outstanding DMA before each LDS read.
 //    - Registers (128x128 tiles): K-tiles of 128 bytes per row are loaded into registers one
@@ -102,8 +103,11 @@ __device__ inline void dma16(const u32x4& desc, int voff, int soff, unsigned lds
                : "memory", "m0");
 }
 
-// XOR key of the DMA pipeline's LDS layout: 16-byte slot of chunk c in row r is c ^ swz(r).
-__device__ constexpr int swz(int r) { return (r >> 2) & 3; }
+// XOR key of the DMA pipeline's LDS layout (rows of KB bytes): the 16-byte slot of chunk c in row r
+// is c ^ swz<KB>(r). A ds_read_b128 is served 16 lanes (256 bytes of banks) at a time, and the 16
+// rows one pass reads then land in 16 distinct 16-byte bank groups.
+template <int KB>
+__device__ constexpr int swz(int r) { return (r / (256 / KB)) % (KB / 16); }
 
 template <int N>
 __device__ inline void wait_vmcnt() {
@@ -280,7 +284,7 @@ __device__ inline void dispatch_na(int na, F&& f) {
 // ------------------------------------------------------------------------------------------------
 // DMA pipeline: 256x256 tiles, LDS fed straight from HBM, three K-tiles in flight
 // ------------------------------------------------------------------------------------------------
-template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, Epi EPI>
+template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, int NS, int KB, Epi EPI>
 __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_dma_kernel(GemmArgs p) {
   constexpr int NW = WAVES_M * WAVES_N;
@@ -290,8 +294,8 @@ gemm_dma_kernel(GemmArgs p) {
   static_assert(!GLU || WN % 2 == 0, "GLU needs gate/up column-block pairs");
   constexpr int BNO = GLU ? BNB / 2 : BNB;
   constexpr int WNO = GLU ? WN / 2 : WN;
-  constexpr int NS = 4;                    // LDS stages
-  constexpr int KB = 64;                   // bytes of every row per K-tile
+  // NS LDS stages of KB bytes of every row per K-tile
+  static_assert(NS >= 2 && NS <= 5 && (KB == 64 || KB == 128), "pipeline shape");
   constexpr int RPD = 1024 / KB;           // rows per 1 KB DMA block
   constexpr int A_PW = BM / RPD / NW;      // DMA blocks per wave per K-tile
   constexpr int B_PW = BNB / RPD / NW;
@@ -327,13 +331,13 @@ gemm_dma_kernel(GemmArgs p) {
   const int KT1 = p.K1 * (int)sizeof(TI) / KB;
 
   // The lane's source chunk for each DMA block of this wave (swizzled so that LDS slot s of row r
-  // holds chunk s ^ swz(r)). A gathered row outside A gets an offset past the buffer end.
-  const int lr = lane >> 2, slot = lane & 3;
+  // holds chunk s ^ swz<KB>(r)). A gathered row outside A gets an offset past the buffer end.
+  const int lr = lane / (KB / 16), slot = lane % (KB / 16);
   int a_voff[A_PW], b_voff[B_PW], a2_voff[A_PW], b2_voff[B_PW];
 #pragma unroll
   for (int i = 0; i < A_PW; ++i) {
     const int r = (wave * A_PW + i) * RPD + lr;
-    const int ch = (slot ^ swz(r)) * 16;
+    const int ch = (slot ^ swz<KB>(r)) * 16;
     if (gather) {
       const int src = r < t.rows ? p.a_rows[t.row0 + r] : -1;
       a_voff[i] = (src >= 0 && src < p.a_nrows) ? src * (int)a_ld + ch : kOutOfRange;
@@ -345,7 +349,7 @@ gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
   for (int i = 0; i < B_PW; ++i) {
     const int r = (wave * B_PW + i) * RPD + lr;
-    const int ch = (slot ^ swz(r)) * 16;
+    const int ch = (slot ^ swz<KB>(r)) * 16;
     b_voff[i] = (r % BNO) * (int)b_ld + ch;
     b2_voff[i] = (r % BNO) * (int)b_ld2 + ch;
   }
@@ -375,35 +379,36 @@ gemm_dma_kernel(GemmArgs p) {
   };
   constexpr int PER_TILE = A_PW + B_PW;  // DMA instructions per wave per K-tile
   auto wait_tiles_after = [&](int n) __attribute__((always_inline)) {
-    static_assert(NS == 4, "waits below cover up to two younger K-tiles");
-    if (n >= 2) wait_vmcnt<2 * PER_TILE>();
-    else if (n == 1) wait_vmcnt<PER_TILE>();
+    if (NS > 4 && n >= 3) wait_vmcnt<3 * PER_TILE>();
+    else if (NS > 3 && n == 2) wait_vmcnt<2 * PER_TILE>();
+    else if (NS > 2 && n == 1) wait_vmcnt<PER_TILE>();
     else wait_vmcnt<0>();
   };
 
   f32x16 acc[WM][WN];
   zero_acc(acc);
-  // fragment offsets for the two 32-byte k-steps of a K-tile (row-block base added per block)
-  const int sw = swz(lane & 31);  // row-block bases are multiples of 32, so only lane & 31 matters
-  const int fo0 = (lane & 31) * KB + (((lane >> 5) ^ sw) * 16);
-  const int fo1 = (lane & 31) * KB + (((2 + (lane >> 5)) ^ sw) * 16);
+  // fragment offset of each 32-byte k-step of a K-tile (row-block bases, multiples of 32 rows, keep
+  // the swizzle key of row lane & 31)
+  constexpr int KS = KB / 32;
+  int fo[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) fo[s] = (lane & 31) * KB + (((2 * s + (lane >> 5)) ^ swz<KB>(lane & 31)) * 16);
 
   dispatch_na<WM>(na, [&](auto na_c) __attribute__((always_inline)) {
     constexpr int NA = decltype(na_c)::value;
     auto compute = [&](int stage) __attribute__((always_inline)) {
       const char* base = smem + stage * STAGE;
 #pragma unroll
-      for (int s = 0; s < KB / 32; ++s) {
-        const int fo = s == 0 ? fo0 : fo1;
+      for (int s = 0; s < KS; ++s) {
         uint4 af[NA > 0 ? NA : 1], bf[WN];
 #pragma unroll
         for (int i = 0; i < NA; ++i)
-          af[i] = *reinterpret_cast<const uint4*>(base + (i * WAVES_M + wm) * 32 * KB + fo);
+          af[i] = *reinterpret_cast<const uint4*>(base + (i * WAVES_M + wm) * 32 * KB + fo[s]);
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
           const int ocb = (j % WNO) * WAVES_N + wn;
           const int bblk = (GLU && j >= WNO) ? BNO / 32 + ocb : ocb;
-          bf[j] = *reinterpret_cast<const uint4*>(base + A_BYTES + bblk * 32 * KB + fo);
+          bf[j] = *reinterpret_cast<const uint4*>(base + A_BYTES + bblk * 32 * KB + fo[s]);
         }
 #pragma unroll
         for (int i = 0; i < NA; ++i)
@@ -596,13 +601,16 @@ int64_t grid_blocks(const GemmArgs& a, Epi epi) {
     case Epi::AddF32: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, Epi::AddF32>), grid, block, 0, s, a); break;       \
   }
 
+constexpr int kDmaStages = 2;    // LDS stages of the DMA pipeline
+constexpr int kDmaKBytes = 128;  // bytes of every row per K-tile (64 bf16)
+
 template <typename TI>
 hipError_t launch_big(const GemmArgs& a, Epi epi, hipStream_t s) {
   const int64_t blocks = grid_blocks<256, 256>(a, epi);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(8 * kWave);
-  LMOE_LAUNCH_EPI(gemm_dma_kernel, TI, 2, 4, 4, 2)
+  LMOE_LAUNCH_EPI(gemm_dma_kernel, TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes)
   return hipGetLastError();
 }
 
