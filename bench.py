@@ -56,6 +56,56 @@ def glu_bytes(cfg, offsets) -> tuple[float, float]:
     return float(w_bytes + a_bytes + h_bytes), flops
 
 
+def kernel_work(cfg, offsets, fused: bool = True) -> dict:
+    """Algorithmic work of each kernel for one forward: ("mfma", FLOPs) for the contractions,
+    ("hbm", bytes) for the rest. GEMM FLOPs count only real rows; routed weights count only the
+    experts that received tokens."""
+    import numpy as np
+
+    T, D, L, E, k, I = cfg.T, cfg.d_model, cfg.d_latent, cfg.n_experts, cfg.top_k, cfg.inter
+    S, Is, NB = cfg.n_shared, cfg.inter_shared, cfg.n_bins
+    esz = 2 if cfg.act_dtype == "bf16" else 4
+    counts = np.diff(offsets)
+    touched = int((counts > 0).sum())
+    rows = int(offsets[-1])
+    glu_b, _ = glu_bytes(cfg, offsets)
+    work = {
+        "router_split": ("hbm", E * D * (4 + 6)),
+        "gemm_router": ("mfma", (3 if esz == 2 else 1) * 2.0 * T * D * E),
+        "route_topk": ("hbm", T * E * 4 + E * 4 + T * k * 8 + T * 8),
+        "qb_hist": ("hbm", T * E * 4 + E * 4 + T * 8 + T * k * 4 + E * NB * 4 * 2),
+        "gemm_down": ("mfma", 2.0 * T * D * L),
+        "perm_count": ("hbm", T * k * 4),
+        "perm_scatter": ("hbm", T * k * 12),
+        "gemm_glu_grouped": ("hbm", glu_b),
+        "gemm_down_grouped": ("hbm", touched * L * I * esz + rows * (I + L) * esz),
+        "gemm_glu_dense": ("mfma", 2.0 * T * D * 2 * S * Is),
+        "gemm_out_dense": ("mfma", 2.0 * T * S * Is * D),
+        "combine_norm": ("hbm", rows * L * esz + T * k * 8 + L * 4 + T * L * esz),
+        "gemm_up": ("mfma", 2.0 * T * (L + (S * Is if fused else 0)) * D),
+        "qb_update": ("hbm", E * NB * 4 * 2 + E * 8),
+    }
+    return work
+
+
+def kernel_roofline(work: dict, kernels_ms: dict) -> dict:
+    """Each kernel's achieved rate against the peak of the unit that bounds it."""
+    out = {}
+    for name, (bound, amount) in work.items():
+        ms = kernels_ms.get(name)
+        if not ms:
+            continue
+        if bound == "mfma":
+            tf = amount / (ms * 1e-3) / 1e12
+            out[name] = {"bound": "mfma", "achieved": round(tf, 1), "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+        else:
+            gbs = amount / (ms * 1e-3) / 1e9
+            out[name] = {"bound": "hbm", "achieved": round(gbs, 1), "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def cpu_baseline(cfg, inp, sample_tokens: int) -> dict:
     """The oracle as it stands, on a bounded sample of the same workload (host cores)."""
     import numpy as np
@@ -200,6 +250,7 @@ def main() -> int:
                      "mfma_tflops": round(flops / avg_s / 1e12, 1),
                      "mfma_frac": round(flops / avg_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "kernels_ms_per_step": kernels,
+        "kernels_roofline": kernel_roofline(kernel_work(cfg, offsets, layer.fused), kernels),
     }
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on {args.cpu_sample} tokens")

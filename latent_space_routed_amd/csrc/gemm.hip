@@ -398,22 +398,29 @@ gemm_dma_kernel(GemmArgs p) {
     constexpr int NA = decltype(na_c)::value;
     auto compute = [&](int stage) __attribute__((always_inline)) {
       const char* base = smem + stage * STAGE;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        uint4 af[NA > 0 ? NA : 1], bf[WN];
+      // fragments of k-step s + 1 are read from LDS while the MFMAs of k-step s run
+      uint4 af[2][NA > 0 ? NA : 1], bf[2][WN];
+      auto load = [&](int s, uint4 (&a)[NA > 0 ? NA : 1], uint4 (&b)[WN]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < NA; ++i)
-          af[i] = *reinterpret_cast<const uint4*>(base + (i * WAVES_M + wm) * 32 * KB + fo[s]);
+          a[i] = *reinterpret_cast<const uint4*>(base + (i * WAVES_M + wm) * 32 * KB + fo[s]);
 #pragma unroll
         for (int j = 0; j < WN; ++j) {
           const int ocb = (j % WNO) * WAVES_N + wn;
           const int bblk = (GLU && j >= WNO) ? BNO / 32 + ocb : ocb;
-          bf[j] = *reinterpret_cast<const uint4*>(base + A_BYTES + bblk * 32 * KB + fo[s]);
+          b[j] = *reinterpret_cast<const uint4*>(base + A_BYTES + bblk * 32 * KB + fo[s]);
         }
+      };
+      load(0, af[0], bf[0]);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) load(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NA; ++i)
 #pragma unroll
-          for (int j = 0; j < WN; ++j) Mfma<TI>::run(acc[i][j], af[i], bf[j]);
+          for (int j = 0; j < WN; ++j) Mfma<TI>::run(acc[i][j], af[s & 1][i], bf[s & 1][j]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     const int pre = min(KT, NS - 1);
