@@ -207,7 +207,7 @@ def main() -> int:
 
     names = ["router_split", "gemm_router", "route_topk", "qb_hist", "gemm_down", "perm_count", "perm_scan",
              "perm_scatter", "gather_rows", "mtile_prefix", "gemm_glu_grouped", "gemm_down_grouped",
-             "gemm_glu_dense", "gemm_out_dense", "combine_norm", "gemm_up", "qb_update"]
+             "gemm_glu_dense", "gemm_out_dense", "combine_norm", "gemm_up", "splitk_reduce", "qb_update"]
     kernels = {}
     for n in names:
         cnt, ms = _lib.profile_get(n)

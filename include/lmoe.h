@@ -55,10 +55,15 @@ typedef struct {
  * inter_shared multiples of 64, n_experts <= 2048, top_k <= 64, n_bins in [2, 32768] and a latent
  * row of at most 16 KiB (d_latent <= 8192 in bf16, 4096 in f32), else LMOE_ERR_UNSUPPORTED. */
 
-enum { LMOE_CALL_ROUTE = 0, LMOE_CALL_PERMUTE = 1, LMOE_CALL_GROUPED_GLU = 2 };
+enum { LMOE_CALL_ROUTE = 0, LMOE_CALL_PERMUTE = 1, LMOE_CALL_GROUPED_GLU = 2, LMOE_CALL_COMBINE_NORM_UP = 3 };
 
 /* Bytes of workspace `which_call` needs for this shape (0 when none). For LMOE_CALL_GROUPED_GLU
- * the value covers any group count up to max(n_experts, 1). */
+ * the value covers any group count up to max(n_experts, 1) and the shared-expert call.
+ * Small batches (whose dense GEMMs would occupy fewer than half the CUs) split the contraction
+ * dimension and sum f32 partial products in the workspace; the returned size includes that space.
+ * A call given less than the returned size but at least its own minimum (the tile list, the router
+ * weight split, the permutation counts) runs its dense GEMMs unsplit: same results up to f32
+ * summation order, slower on small batches. */
 size_t lmoe_workspace_bytes(const lmoe_shape* shape, int which_call);
 
 /* Human-readable name of a status. */
@@ -135,7 +140,7 @@ lmoe_status lmoe_permute(const lmoe_shape* shape, const void* x, const void* w_d
  *   w2            [G, n_out, inter] act_dtype, or NULL to stop after h (y is then unused)
  *   h             [rows, inter] act_dtype (out)
  *   y             [rows, n_out] y_dtype (out; y_dtype is LMOE_F32 or act_dtype)
- *   workspace     LMOE_CALL_GROUPED_GLU bytes (device tile list)
+ *   workspace     LMOE_CALL_GROUPED_GLU bytes (device tile list; split-K partials for one group)
  * With a_row_index, a must be under 2 GiB (31-bit byte offsets; LMOE_ERR_UNSUPPORTED otherwise). */
 lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* shape, int32_t n_groups, int32_t rows, int32_t K,
                                   int32_t inter, int32_t n_out, const void* a, int32_t a_rows,
@@ -166,11 +171,13 @@ lmoe_status lmoe_pack_shared(const lmoe_shape* shape, const void* w1s, const voi
  *                                         w2_shared]^T accumulates both products in one f32 sum
  *   n_out        [T, L] act_dtype (out)   n = gamma * z / sqrt(mean(z^2) + eps), z = sum_j w_tj y(t,j)
  *   out          [T, D] out_dtype (out)   n . w_up^T + shared part, rounded once from the f32
- *                                         accumulator; out_dtype is LMOE_F32 or act_dtype           */
+ *                                         accumulator; out_dtype is LMOE_F32 or act_dtype
+ *   workspace    LMOE_CALL_COMBINE_NORM_UP bytes, or NULL (no split-K for small batches)          */
 lmoe_status lmoe_combine_norm_up(const lmoe_shape* shape, const void* y_perm, const int32_t* slot_of_pair,
                                  const float* topk_w, const float* gamma, const void* w_up,
                                  const float* y_shared, const void* h_shared, const void* w2_shared,
-                                 void* n_out, void* out, int32_t out_dtype, void* stream);
+                                 void* n_out, void* out, int32_t out_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* Kernel timing for measurement. When enabled, every kernel the library enqueues is bracketed by
  * HIP events on its stream. lmoe_profile_collect() synchronises those events and folds them into

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "liblmoe.so")
 
 LMOE_OK, LMOE_ERR_INVALID_ARGUMENT, LMOE_ERR_UNSUPPORTED, LMOE_ERR_WORKSPACE, LMOE_ERR_HIP = range(5)
 LMOE_F32, LMOE_BF16 = 0, 1
-LMOE_CALL_ROUTE, LMOE_CALL_PERMUTE, LMOE_CALL_GROUPED_GLU = 0, 1, 2
+LMOE_CALL_ROUTE, LMOE_CALL_PERMUTE, LMOE_CALL_GROUPED_GLU, LMOE_CALL_COMBINE_NORM_UP = 0, 1, 2, 3
 
 # every symbol include/lmoe.h declares
 EXPORTS = ("lmoe_workspace_bytes", "lmoe_status_string", "lmoe_route", "lmoe_qb_histogram", "lmoe_qb_update",
@@ -68,7 +68,7 @@ def lib() -> ctypes.CDLL:
                                                      _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
             "lmoe_pack_shared": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
             "lmoe_combine_norm_up": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
-                                                    _P]),
+                                                    _P, ctypes.c_size_t, _P]),
             "lmoe_profile_enable": (None, [ctypes.c_int]),
             "lmoe_profile_reset": (None, []),
             "lmoe_profile_collect": (ctypes.c_int, []),
@@ -158,12 +158,13 @@ def lmoe_pack_shared(shape, w1s, w2s, w1s_packed, w2s_packed, stream=None):
 
 
 def lmoe_combine_norm_up(shape, y_perm, slot_of_pair, topk_w, gamma, w_up, y_shared, n_out, out, h_shared=None,
-                         w2_shared=None, stream=None):
+                         w2_shared=None, workspace=None, stream=None):
     out_dtype = LMOE_F32 if out.dtype == torch.float32 else LMOE_BF16
     _check("lmoe_combine_norm_up",
            lib().lmoe_combine_norm_up(ctypes.byref(shape), _ptr(y_perm), _ptr(slot_of_pair), _ptr(topk_w),
                                       _ptr(gamma), _ptr(w_up), _ptr(y_shared), _ptr(h_shared), _ptr(w2_shared),
-                                      _ptr(n_out), _ptr(out), out_dtype, _stream(stream)))
+                                      _ptr(n_out), _ptr(out), out_dtype, _ptr(workspace), _nbytes(workspace),
+                                      _stream(stream)))
 
 
 def profile_enable(on: bool) -> None:

@@ -58,6 +58,47 @@ size_t permute_ws(const lmoe_shape* sh) {
 }
 size_t glu_ws(int groups) { return round_up((size_t)(groups + 1) * 4); }
 
+// Split-K plans of the dense GEMMs behind each call (no split once the batch fills the chip).
+SplitPlan router_plan(const lmoe_shape* sh) {
+  const int D = sh->d_model;
+  return plan_split_k(sh->T, sh->n_experts, sh->act_dtype == LMOE_BF16 ? 3 * D : D, 0, D, esize(sh->act_dtype));
+}
+SplitPlan down_plan(const lmoe_shape* sh) {
+  return plan_split_k(sh->T, sh->d_latent, sh->d_model, 0, sh->d_model, esize(sh->act_dtype));
+}
+SplitPlan up_plan(const lmoe_shape* sh, bool shared_folded) {
+  const int Ss = sh->n_shared * sh->inter_shared;
+  return plan_split_k(sh->T, sh->d_model, sh->d_latent, shared_folded ? Ss : 0, sh->d_latent, esize(sh->act_dtype));
+}
+size_t split_bytes(const SplitPlan& sp, int64_t M, int64_t n_cols) { return round_up(split_k_bytes(sp, M, n_cols)); }
+size_t shared_split_bytes(const lmoe_shape* sh) {
+  const int Ss = sh->n_shared * sh->inter_shared;
+  if (Ss < 64) return 0;
+  const int esz = esize(sh->act_dtype);
+  const size_t g1 = split_bytes(plan_split_k(sh->T, 2 * (int64_t)Ss, sh->d_model, 0, sh->d_model, esz), sh->T, 2 * (int64_t)Ss);
+  const size_t g2 = split_bytes(plan_split_k(sh->T, sh->d_model, Ss, 0, Ss, esz), sh->T, sh->d_model);
+  return g1 > g2 ? g1 : g2;
+}
+size_t combine_split_bytes(const lmoe_shape* sh) {
+  const size_t a = split_bytes(up_plan(sh, false), sh->T, sh->d_model);
+  const size_t b = sh->n_shared * sh->inter_shared >= 64 ? split_bytes(up_plan(sh, true), sh->T, sh->d_model) : 0;
+  return a > b ? a : b;
+}
+
+// The partial-product region after the call's own workspace (at offset `base`), or nullptr when the
+// plan has no split or the caller's workspace does not hold it (the GEMM then runs unsplit).
+float* split_region(const SplitPlan& sp, int64_t M, int64_t n_cols, void* workspace, size_t workspace_bytes,
+                    size_t base) {
+  if (sp.splits < 2 || !workspace || !aligned16(workspace)) return nullptr;
+  if (workspace_bytes < base + split_k_bytes(sp, M, n_cols)) return nullptr;
+  return reinterpret_cast<float*>(static_cast<char*>(workspace) + base);
+}
+
+hipError_t run_gemm(const GemmArgs& a, int dtype, Epi epi, GemmShape shape, const SplitPlan& sp, float* part,
+                    hipStream_t s) {
+  return part ? launch_gemm_split(a, dtype, epi, sp, part, s) : launch_gemm(a, dtype, epi, shape, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -76,9 +117,10 @@ const char* lmoe_status_string(lmoe_status s) {
 size_t lmoe_workspace_bytes(const lmoe_shape* sh, int which) {
   if (check_shape(sh) != LMOE_OK) return 0;
   switch (which) {
-    case LMOE_CALL_ROUTE: return route_ws(sh);
-    case LMOE_CALL_PERMUTE: return permute_ws(sh);
-    case LMOE_CALL_GROUPED_GLU: return glu_ws(sh->n_experts > 1 ? sh->n_experts : 1);
+    case LMOE_CALL_ROUTE: return route_ws(sh) + split_bytes(router_plan(sh), sh->T, sh->n_experts);
+    case LMOE_CALL_PERMUTE: return permute_ws(sh) + split_bytes(down_plan(sh), sh->T, sh->d_latent);
+    case LMOE_CALL_GROUPED_GLU: return glu_ws(sh->n_experts > 1 ? sh->n_experts : 1) + shared_split_bytes(sh);
+    case LMOE_CALL_COMBINE_NORM_UP: return combine_split_bytes(sh);
   }
   return 0;
 }
@@ -119,7 +161,9 @@ lmoe_status lmoe_route(const lmoe_shape* sh, const void* x, const float* w_route
     a.ldb = D;
     a.K = D;
   }
-  st = hip_status(launch_gemm(a, sh->act_dtype, Epi::Sigmoid, dense_shape(T, ceil_div(E, 256)), s));
+  const SplitPlan sp = router_plan(sh);
+  float* part = split_region(sp, T, E, workspace, workspace_bytes, need);
+  st = hip_status(run_gemm(a, sh->act_dtype, Epi::Sigmoid, dense_shape(T, ceil_div(E, 256)), sp, part, s));
   if (st != LMOE_OK) return st;
   return hip_status(launch_topk(scores, bias, T, E, sh->top_k, topk_idx, topk_w, thresh, s));
 }
@@ -174,7 +218,9 @@ lmoe_status lmoe_permute(const lmoe_shape* sh, const void* x, const void* w_down
   a.N = L;
   a.K = D;
   a.tag = "gemm_down";
-  st = hip_status(launch_gemm(a, sh->act_dtype, Epi::Store, dense_shape(T, ceil_div(L, 256)), s));
+  const SplitPlan sp = down_plan(sh);
+  float* part = split_region(sp, T, L, workspace, workspace_bytes, need);
+  st = hip_status(run_gemm(a, sh->act_dtype, Epi::Store, dense_shape(T, ceil_div(L, 256)), sp, part, s));
   if (st != LMOE_OK) return st;
   st = hip_status(launch_permute(topk_idx, T, E, k, expert_offsets, sorted_token, slot_of_pair,
                                  static_cast<int32_t*>(workspace), s));
@@ -237,7 +283,18 @@ lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* sh, int32_t G, int32_t rows,
   g1.beta1 = sh->beta1;
   g1.beta2 = sh->beta2;
   g1.tag = group_offsets ? "gemm_glu_grouped" : "gemm_glu_dense";
-  st = hip_status(launch_gemm(g1, dt, Epi::Glu, shape, s));
+  const size_t base = round_up(need);
+  SplitPlan sp1, sp2;
+  float *part1 = nullptr, *part2 = nullptr;
+  if (!group_offsets && !a_row_index) {
+    sp1 = plan_split_k(rows, 2 * (int64_t)inter, K, 0, K, esize(dt));
+    part1 = split_region(sp1, rows, 2 * (int64_t)inter, workspace, workspace_bytes, base);
+    if (w2) {
+      sp2 = plan_split_k(rows, n_out, inter, 0, inter, esize(dt));
+      part2 = split_region(sp2, rows, n_out, workspace, workspace_bytes, base);
+    }
+  }
+  st = hip_status(run_gemm(g1, dt, Epi::Glu, shape, sp1, part1, s));
   if (st != LMOE_OK || !w2) return st;
 
   GemmArgs g2 = g1;
@@ -256,7 +313,7 @@ lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* sh, int32_t G, int32_t rows,
   g2.K = inter;
   g2.tag = group_offsets ? "gemm_down_grouped" : "gemm_out_dense";
   if (!group_offsets) shape = dense_shape(rows, ceil_div(n_out, 256));
-  return hip_status(launch_gemm(g2, dt, Epi::Store, shape, s));
+  return hip_status(run_gemm(g2, dt, Epi::Store, shape, sp2, part2, s));
 }
 
 lmoe_status lmoe_pack_shared(const lmoe_shape* sh, const void* w1s, const void* w2s, void* w1s_packed,
@@ -273,7 +330,7 @@ lmoe_status lmoe_pack_shared(const lmoe_shape* sh, const void* w1s, const void* 
 lmoe_status lmoe_combine_norm_up(const lmoe_shape* sh, const void* y_perm, const int32_t* slot_of_pair,
                                  const float* topk_w, const float* gamma, const void* w_up, const float* y_shared,
                                  const void* h_shared, const void* w2_shared, void* n_out, void* out,
-                                 int32_t out_dtype, void* stream) {
+                                 int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   lmoe_status st = check_shape(sh);
   if (st != LMOE_OK) return st;
   if (out_dtype != LMOE_F32 && out_dtype != sh->act_dtype) return LMOE_ERR_INVALID_ARGUMENT;
@@ -314,8 +371,10 @@ lmoe_status lmoe_combine_norm_up(const lmoe_shape* sh, const void* y_perm, const
     a.K1 = L;
     a.K = L + Ss;
   }
-  return hip_status(
-      launch_gemm(a, sh->act_dtype, y_shared ? Epi::AddF32 : Epi::Store, dense_shape(T, ceil_div(D, 256)), s));
+  const SplitPlan sp = up_plan(sh, h_shared != nullptr);
+  float* part = split_region(sp, T, D, workspace, workspace_bytes, 0);
+  return hip_status(run_gemm(a, sh->act_dtype, y_shared ? Epi::AddF32 : Epi::Store, dense_shape(T, ceil_div(D, 256)),
+                             sp, part, s));
 }
 
 }  // extern "C"

@@ -113,7 +113,25 @@ struct GemmArgs {
   const void* B2;
   int64_t ldb2;
   int K1;
+  // Split-K (register pipeline, dense): workgroup row blockIdx.y = s multiplies K-chunk s (K
+  // elements) of the concatenated range [0, K1) of A/B then [K1, ...) of A2/B2, and stores its f32
+  // partial product at C + s * c_split. splits <= 1: no split.
+  int splits;
+  int64_t c_split;
 };
+
+// K-split of a dense GEMM on few rows (decode-size batches), so that its register-pipeline tiles
+// occupy every CU; the partial products are then summed by a reduction that applies the epilogue.
+struct SplitPlan {
+  int splits = 1;  // 1 = no split
+  int chunk = 0;   // K elements per split
+};
+SplitPlan plan_split_k(int64_t M, int64_t n_cols, int K1, int K2, int a_kwrap, int esz);
+size_t split_k_bytes(const SplitPlan& sp, int64_t M, int64_t n_cols);
+// Runs a (dense, non-gathered) GEMM as the planned split plus the reducing epilogue; partials holds
+// split_k_bytes() bytes.
+hipError_t launch_gemm_split(const GemmArgs& a, int in_dtype, Epi epi, const SplitPlan& sp, float* partials,
+                             hipStream_t s);
 
 enum class GemmShape : int { Big = 0, Small = 1 };
 

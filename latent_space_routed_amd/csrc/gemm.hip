@@ -455,7 +455,24 @@ gemm_dma_kernel(GemmArgs p) {
 constexpr int kRowPitch = 144;
 
 template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, Epi EPI>
-__global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_reg_kernel(GemmArgs p) {
+__global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_reg_kernel(GemmArgs p_in) {
+  GemmArgs p = p_in;
+  if (p.splits > 1) {  // this workgroup's K-chunk, as a plain GEMM over K = chunk into its own partial
+    const int s = blockIdx.y, s1 = p.K1 / p.K;
+    if (s < s1) {
+      p.A = static_cast<const char*>(p.A) + (int64_t)((s * p.K) % p.a_kwrap) * (int64_t)sizeof(TI);
+      p.B = static_cast<const char*>(p.B) + (int64_t)s * p.K * (int64_t)sizeof(TI);
+    } else {
+      p.A = static_cast<const char*>(p.A2) + (int64_t)(s - s1) * p.K * (int64_t)sizeof(TI);
+      p.lda = p.lda2;
+      p.B = static_cast<const char*>(p.B2) + (int64_t)(s - s1) * p.K * (int64_t)sizeof(TI);
+      p.ldb = p.ldb2;
+    }
+    p.A2 = nullptr;
+    p.K1 = p.K;
+    p.a_kwrap = p.K;
+    p.C = static_cast<float*>(p.C) + s * p.c_split;
+  }
   constexpr int NT = WAVES_M * WAVES_N * kWave;
   constexpr int BM = WAVES_M * WM * 32;
   constexpr int BNB = WAVES_N * WN * 32;
@@ -589,6 +606,63 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_reg_kernel(GemmA
   epilogue<TI, WAVES_M, WAVES_N, WM, WN, EPI>(p, t, acc, wm, wn, lane, na);
 }
 
+// Sums the split-K partials (in split order) and applies the epilogue of the unsplit GEMM; four
+// consecutive outputs of one row per thread. GLU partials hold the gate columns, then the up columns.
+template <Epi EPI, bool ACCURATE>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs p, const float* __restrict__ part, int splits,
+                                                            int64_t stride, int n_cols) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (int64_t)p.M * p.N) return;
+  const int64_t m = i / p.N;
+  const int c = (int)(i - m * p.N);
+  float v[4] = {0.0f, 0.0f, 0.0f, 0.0f}, u[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float* pr = part + m * n_cols + c;
+  for (int s = 0; s < splits; ++s) {
+    const float4 a = *reinterpret_cast<const float4*>(pr + s * stride);
+    v[0] += a.x;
+    v[1] += a.y;
+    v[2] += a.z;
+    v[3] += a.w;
+    if constexpr (EPI == Epi::Glu) {
+      const float4 b = *reinterpret_cast<const float4*>(pr + s * stride + p.N);
+      u[0] += b.x;
+      u[1] += b.y;
+      u[2] += b.z;
+      u[3] += b.w;
+    }
+  }
+  const float inv_b1 = 1.0f / p.beta1, inv_b2 = 1.0f / p.beta2;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t off = m * p.ldc + c + q;
+    if constexpr (EPI == Epi::Store) {
+      store_out(p, off, v[q]);
+    } else if constexpr (EPI == Epi::Glu) {
+      store_out(p, off, situ_glu<ACCURATE>(v[q], u[q], p.beta1, inv_b1, p.beta2, inv_b2));
+    } else if constexpr (EPI == Epi::Sigmoid) {
+      const float x = v[q] + (p.col_bias ? p.col_bias[c + q] : 0.0f);
+      static_cast<float*>(p.C)[off] = 1.0f / (1.0f + expf(-x));
+    } else {
+      store_out(p, off, v[q] + p.residual[m * p.ldr + c + q]);
+    }
+  }
+}
+
+template <Epi EPI, bool ACCURATE>
+void launch_reduce(dim3 grid, hipStream_t s, const GemmArgs& a, const float* part, int splits, int64_t stride,
+                   int n_cols) {
+  hipLaunchKernelGGL((splitk_reduce_kernel<EPI, ACCURATE>), grid, dim3(256), 0, s, a, part, splits, stride, n_cols);
+}
+
+int gcd_int(int a, int b) {
+  while (b) {
+    const int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
 // ------------------------------------------------------------------------------------------------
 // launch
 // ------------------------------------------------------------------------------------------------
@@ -660,6 +734,85 @@ __global__ void __launch_bounds__(1024) mtile_prefix_kernel(const int32_t* goff,
 }  // namespace
 
 int gemm_block_m(GemmShape shape) { return shape == GemmShape::Big ? 256 : 128; }
+
+// Split only when the 128x128 tiles cover less than half the CUs: the largest K-chunk (whole
+// register K-tiles, at least four, dividing both K segments and the A wrap period) that gives about
+// 256 workgroups, at most 64 splits.
+SplitPlan plan_split_k(int64_t M, int64_t n_cols, int K1, int K2, int a_kwrap, int esz) {
+  SplitPlan none;
+  if (M <= 0 || n_cols <= 0 || n_cols % 4 != 0 || K1 <= 0 || K2 < 0 || a_kwrap <= 0) return none;
+  const int64_t tiles = ceil_div(M, 128) * ceil_div(n_cols, 128);
+  if (tiles >= 128) return none;
+  const int gran = 128 / esz;  // elements of one register K-tile
+  int g = gcd_int(K1, a_kwrap);
+  if (K2 > 0) g = gcd_int(g, K2);
+  if (g % gran) return none;
+  const int want = (int)ceil_div(256, tiles);
+  SplitPlan best;
+  for (int c = g; c >= 4 * gran; c -= gran) {
+    if (g % c) continue;
+    const int n = (K1 + K2) / c;
+    if (n > 64) break;
+    best.splits = n;
+    best.chunk = c;
+    if (n >= want) break;
+  }
+  return best.splits >= 2 ? best : none;
+}
+
+size_t split_k_bytes(const SplitPlan& sp, int64_t M, int64_t n_cols) {
+  return sp.splits > 1 ? (size_t)sp.splits * (size_t)M * (size_t)n_cols * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_split(const GemmArgs& a, int in_dtype, Epi epi, const SplitPlan& sp, float* partials,
+                             hipStream_t s) {
+  const bool glu = epi == Epi::Glu;
+  const int n_cols = glu ? 2 * a.N : a.N;
+  if (sp.splits < 2 || a.goff || a.a_rows || (glu && a.glu_up_off != a.N)) return hipErrorInvalidValue;
+  GemmArgs q = a;
+  q.K1 = a.A2 ? a.K1 : a.K;  // end of the first K segment
+  q.K = sp.chunk;
+  q.splits = sp.splits;
+  q.c_split = (int64_t)a.M * n_cols;
+  q.C = partials;
+  q.ldc = n_cols;
+  q.c_dtype = LMOE_F32;
+  q.N = n_cols;
+  q.col_bias = nullptr;
+  q.residual = nullptr;
+  {
+    KernelTimer timer(a.tag ? a.tag : "gemm", s);
+    const int64_t blocks = grid_blocks<128, 128>(q, Epi::Store);
+    if (blocks <= 0) return hipSuccess;
+    const dim3 grid((unsigned)blocks, (unsigned)sp.splits), block(4 * kWave);
+    if (in_dtype == LMOE_BF16)
+      hipLaunchKernelGGL((gemm_reg_kernel<uint16_t, 2, 2, 2, 2, Epi::Store>), grid, block, 0, s, q);
+    else
+      hipLaunchKernelGGL((gemm_reg_kernel<float, 2, 2, 2, 2, Epi::Store>), grid, block, 0, s, q);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  KernelTimer timer("splitk_reduce", s);
+  const int64_t quads = (int64_t)a.M * a.N / 4;
+  const dim3 grid((unsigned)ceil_div(quads, 256));
+  const int64_t stride = q.c_split;
+  if (in_dtype == LMOE_F32) {
+    switch (epi) {
+      case Epi::Store: launch_reduce<Epi::Store, true>(grid, s, a, partials, sp.splits, stride, n_cols); break;
+      case Epi::Glu: launch_reduce<Epi::Glu, true>(grid, s, a, partials, sp.splits, stride, n_cols); break;
+      case Epi::Sigmoid: launch_reduce<Epi::Sigmoid, true>(grid, s, a, partials, sp.splits, stride, n_cols); break;
+      case Epi::AddF32: launch_reduce<Epi::AddF32, true>(grid, s, a, partials, sp.splits, stride, n_cols); break;
+    }
+  } else {
+    switch (epi) {
+      case Epi::Store: launch_reduce<Epi::Store, false>(grid, s, a, partials, sp.splits, stride, n_cols); break;
+      case Epi::Glu: launch_reduce<Epi::Glu, false>(grid, s, a, partials, sp.splits, stride, n_cols); break;
+      case Epi::Sigmoid: launch_reduce<Epi::Sigmoid, false>(grid, s, a, partials, sp.splits, stride, n_cols); break;
+      case Epi::AddF32: launch_reduce<Epi::AddF32, false>(grid, s, a, partials, sp.splits, stride, n_cols); break;
+    }
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const GemmArgs& a, int in_dtype, Epi epi, GemmShape shape, hipStream_t s) {
   KernelTimer timer(a.tag ? a.tag : "gemm", s);

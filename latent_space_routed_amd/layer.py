@@ -81,7 +81,7 @@ class LatentMoE:
             "out": torch.empty(T, D, dtype=self.out_dtype, device=dev),
         }
         for name, which in (("ws_route", C.LMOE_CALL_ROUTE), ("ws_permute", C.LMOE_CALL_PERMUTE),
-                            ("ws_glu", C.LMOE_CALL_GROUPED_GLU)):
+                            ("ws_glu", C.LMOE_CALL_GROUPED_GLU), ("ws_combine", C.LMOE_CALL_COMBINE_NORM_UP)):
             n = C.workspace_bytes(shape, which)
             b[name] = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
         self._bufs = b
@@ -123,15 +123,16 @@ class LatentMoE:
             C.lmoe_grouped_situ_glu(shape, 1, T, D, S * Is, D, x, None, self.w1s_packed, None, b["h_s"], None,
                                     b["ws_glu"])
             C.lmoe_combine_norm_up(shape, b["y"], b["slot_of_pair"], b["w"], w.get("gamma"), w["w_up"], None,
-                                   b["n"], b["out"], h_shared=b["h_s"], w2_shared=self.w2s_packed)
+                                   b["n"], b["out"], h_shared=b["h_s"], w2_shared=self.w2s_packed,
+                                   workspace=b["ws_combine"])
         elif S > 0:
             C.lmoe_grouped_situ_glu(shape, 1, T, D, S * Is, D, x, None, self.w1s_packed, self.w2s_packed,
                                     b["h_s"], b["y_sh"], b["ws_glu"])
             C.lmoe_combine_norm_up(shape, b["y"], b["slot_of_pair"], b["w"], w.get("gamma"), w["w_up"], b["y_sh"],
-                                   b["n"], b["out"])
+                                   b["n"], b["out"], workspace=b["ws_combine"])
         else:
             C.lmoe_combine_norm_up(shape, b["y"], b["slot_of_pair"], b["w"], w.get("gamma"), w["w_up"], None,
-                                   b["n"], b["out"])
+                                   b["n"], b["out"], workspace=b["ws_combine"])
         return b
 
     def qb_update(self) -> None:

@@ -46,10 +46,27 @@ def test_workspace_sizes(lib):
     assert C.workspace_bytes(k3, C.LMOE_CALL_ROUTE) == 3 * 896 * 7168 * 2          # bf16 split of W_r
     assert C.workspace_bytes(k3, C.LMOE_CALL_PERMUTE) == 32 * 896 * 4             # per-chunk counts
     assert C.workspace_bytes(k3, C.LMOE_CALL_GROUPED_GLU) == 3840                # tile prefix, rounded
-    assert C.workspace_bytes(C.make_shape(CONFIGS["tiny_f32"]), C.LMOE_CALL_ROUTE) == 0
+    # f32 router: no weight split; 64 tokens x 32 experts split K = 256 in two f32 partials
+    assert C.workspace_bytes(C.make_shape(CONFIGS["tiny_f32"]), C.LMOE_CALL_ROUTE) == 2 * 64 * 32 * 4
+    assert C.workspace_bytes(k3, C.LMOE_CALL_COMBINE_NORM_UP) == 0                # 8192 rows fill the chip
     bad = C.make_shape(CONFIGS["k3_prefill"])
     bad.top_k = bad.n_experts
     assert C.workspace_bytes(bad, C.LMOE_CALL_ROUTE) == 0
+
+
+def test_split_k_workspace_for_small_batches(lib):
+    """A 64-token batch splits the contraction of its dense GEMMs: the workspace grows by whole
+    f32 partial products [splits, T, n_cols] beyond each call's own minimum."""
+    dec = C.make_shape(CONFIGS["k3_decode"])
+    T, D, L, E = 64, 7168, 3584, 896
+    extra = C.workspace_bytes(dec, C.LMOE_CALL_ROUTE) - 3 * E * D * 2
+    assert extra > 0 and extra % (T * E * 4) == 0 and 2 <= extra // (T * E * 4) <= 64
+    # router: chunks divide d_model (the K-wrap of the bf16 split), about 256 workgroups over 7 tiles
+    assert (3 * D) % (3 * D // (extra // (T * E * 4))) == 0 and 7 * (extra // (T * E * 4)) >= 256
+    extra = C.workspace_bytes(dec, C.LMOE_CALL_PERMUTE) - 896 * 4                 # one chunk of E counts
+    assert extra > 0 and extra % (T * L * 4) == 0
+    assert C.workspace_bytes(dec, C.LMOE_CALL_COMBINE_NORM_UP) % (T * D * 4) == 0
+    assert C.workspace_bytes(dec, C.LMOE_CALL_COMBINE_NORM_UP) >= 2 * T * D * 4
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -88,7 +105,7 @@ def test_pointer_validation_before_any_launch(lib):
                                      fake, 0, null, 0, null) == C.LMOE_ERR_INVALID_ARGUMENT
     # combine: y_shared and the folded shared pair are exclusive
     assert lib.lmoe_combine_norm_up(ctypes.byref(sh), fake, fake, fake, null, fake, fake, fake, fake, fake, fake, 0,
-                                    null) == C.LMOE_ERR_INVALID_ARGUMENT
+                                    null, 0, null) == C.LMOE_ERR_INVALID_ARGUMENT
 
 
 def test_empty_batch_is_a_no_op(lib):
@@ -97,4 +114,4 @@ def test_empty_batch_is_a_no_op(lib):
     assert lib.lmoe_route(ctypes.byref(sh), null, null, null, null, null, null, null, null, null, 0, null) == C.LMOE_OK
     assert lib.lmoe_qb_histogram(ctypes.byref(sh), null, null, null, null, null, null) == C.LMOE_OK
     assert lib.lmoe_combine_norm_up(ctypes.byref(sh), null, null, null, null, null, null, null, null, null, null, 0,
-                                    null) == C.LMOE_OK
+                                    null, 0, null) == C.LMOE_OK
