@@ -55,7 +55,12 @@ typedef struct {
  * inter_shared multiples of 64, n_experts <= 2048, top_k <= 64, n_bins in [2, 32768] and a latent
  * row of at most 16 KiB (d_latent <= 8192 in bf16, 4096 in f32), else LMOE_ERR_UNSUPPORTED. */
 
-enum { LMOE_CALL_ROUTE = 0, LMOE_CALL_PERMUTE = 1, LMOE_CALL_GROUPED_GLU = 2, LMOE_CALL_COMBINE_NORM_UP = 3 };
+enum {
+  LMOE_CALL_ROUTE = 0, LMOE_CALL_PERMUTE = 1, LMOE_CALL_GROUPED_GLU = 2, LMOE_CALL_COMBINE_NORM_UP = 3,
+  /* backward calls */
+  LMOE_CALL_BWD_UP = 16, LMOE_CALL_BWD_COMBINE_NORM = 17, LMOE_CALL_BWD_EXPERTS = 18, LMOE_CALL_BWD_DOWN = 19,
+  LMOE_CALL_BWD_SHARED = 20
+};
 
 /* Bytes of workspace `which_call` needs for this shape (0 when none). For LMOE_CALL_GROUPED_GLU
  * the value covers any group count up to max(n_experts, 1) and the shared-expert call.
@@ -178,6 +183,78 @@ lmoe_status lmoe_combine_norm_up(const lmoe_shape* shape, const void* y_perm, co
                                  const float* y_shared, const void* h_shared, const void* w2_shared,
                                  void* n_out, void* out, int32_t out_dtype, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/* ================================================================================================
+ * Backward pass (training). The pages train this layer ([vxz] 01-02, [slm] 训练基础设施) but
+ * print no backward pass; these calls apply the chain rule to the forward above, step by step in
+ * reverse. The quantile-balancing bias selects experts only and has no gradient; the top-k set is
+ * held fixed and the combine weights are differentiated through the unbiased scores.
+ * Storage: the incoming dout and every activation gradient are act_dtype; weight gradients, dgamma,
+ * the router-logit gradients and dx are f32. Each output is written in full (no accumulation into
+ * caller data except dx where stated). Gradients of unselected experts are zero. The forward
+ * tensors are those the forward calls produced for the same batch.
+ * Workspace: lmoe_workspace_bytes(shape, LMOE_CALL_BWD_*); transposed activations live there.
+ * ============================================================================================== */
+
+/* B0: transposed weight copies (the backward contracts over the forward's output dimension).
+ * Re-run after every weight change.
+ *   w1 [E, 2I, L] -> w1_t [E, L, 2I];  w2 [E, L, I] -> w2_t [E, I, L];  w_up [D, L] -> w_up_t [L, D];
+ *   w_down [L, D] -> w_down_t [D, L];  w2s_packed [D, S*I_s] -> w2s_t [S*I_s, D];
+ *   w1s_packed [2*S*I_s, D] -> w1s_t [D, 2*S*I_s]  (the shared pair may both be NULL)           */
+lmoe_status lmoe_bwd_transpose_weights(const lmoe_shape* shape, const void* w1, const void* w2, const void* w_up,
+                                       const void* w2s_packed, const void* w1s_packed, const void* w_down,
+                                       void* w1_t, void* w2_t, void* w_up_t, void* w2s_t, void* w1s_t,
+                                       void* w_down_t, void* stream);
+
+/* B1 (A11 reversed): out = [n | h_s] . [w_up | w2s_packed]^T.
+ *   dout [T, D], n [T, L], h_shared [T, S*I_s] or NULL (then no shared part), w_up_t, w2s_t from B0
+ *   dn [T, L] (out) = dout . w_up;  dh_shared [T, S*I_s] (out) = dout . w2s_packed
+ *   dw_up [D, L] f32 (out) = dout^T n;  dw2_shared [D, S*I_s] f32 (out) = dout^T h_s (packed)   */
+lmoe_status lmoe_bwd_up(const lmoe_shape* shape, const void* dout, const void* n, const void* h_shared,
+                        const void* w_up_t, const void* w2s_t, void* dn, void* dh_shared, float* dw_up,
+                        float* dw2_shared, void* workspace, size_t workspace_bytes, void* stream);
+
+/* B2 (A9 and the combine weights reversed), per token t with z = sum_j w_tj y(t,j) recomputed:
+ *   dz = r gamma dn - (r^3 / L) sum(gamma dn z) z,  r = (mean(z^2) + eps)^-1/2;  dgamma = sum_t dn z r
+ *   dy_perm[slot(t,j)] = w_tj dz;  dw_tj = <dz, y(t,j)>;  S = sum_j s_tj (selected scores);
+ *   dlogit[t,j] = (dw_tj - sum_i w_ti dw_ti) / S * s_tj (1 - s_tj);  dlogit_sorted[slot(t,j)] = the same
+ *   dn [T, L], y_perm [T*k, L], slot_of_pair, topk_idx, scores [T, E], topk_w, gamma: forward tensors
+ *   dy_perm [T*k, L] (out), dlogit [T, k] f32 (out), dlogit_sorted [T*k] f32 (out), dgamma [L] f32 (out) */
+lmoe_status lmoe_bwd_combine_norm(const lmoe_shape* shape, const void* dn, const void* y_perm,
+                                  const int32_t* slot_of_pair, const int32_t* topk_idx, const float* scores,
+                                  const float* topk_w, const float* gamma, void* dy_perm, float* dlogit,
+                                  float* dlogit_sorted, float* dgamma, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* B3 (A1 reversed): logits = x . w_router^T (+ offset).
+ *   dw_router [E, D] f32 (out): row e = sum over expert e's sorted rows r of dlogit_sorted[r] x[sorted_token[r]]
+ *   dx [T, D] f32 (out, overwritten) = sum_j dlogit[t, j] w_router[topk_idx[t, j]]                   */
+lmoe_status lmoe_bwd_router(const lmoe_shape* shape, const void* x, const float* w_router, const float* dlogit,
+                            const float* dlogit_sorted, const int32_t* topk_idx, const int32_t* expert_offsets,
+                            const int32_t* sorted_token, float* dw_router, float* dx, void* stream);
+
+/* B4 (A7 + A8 reversed), rows in expert-sorted order, expert e on rows [off_e, off_{e+1}):
+ *   dh = dy . w2_e (out, [T*k, I]);  dw2_e = dy_e^T h_e (f32 [E, L, I], out)
+ *   [g | u] = x_lat[sorted_token] . w1_e^T recomputed; dgu (out, [T*k, 2I]) = [dg | du] of SiTU-GLU
+ *   dx_perm = dgu . w1_e (out, [T*k, L]);  dw1_e = dgu_e^T x_lat[sorted_token]_e (f32 [E, 2I, L], out)
+ *   x_lat [T, L], sorted_token, expert_offsets, w1, h [T*k, I], dy_perm: forward tensors / B2; w1_t, w2_t: B0 */
+lmoe_status lmoe_bwd_experts(const lmoe_shape* shape, const void* x_lat, const int32_t* sorted_token,
+                             const int32_t* expert_offsets, const void* w1, const void* w1_t, const void* w2_t,
+                             const void* h, const void* dy_perm, void* dh, void* dgu, void* dx_perm, float* dw1,
+                             float* dw2, void* workspace, size_t workspace_bytes, void* stream);
+
+/* B5 (A6 + A5 reversed): dx_lat[t] = sum_j dx_perm[slot(t,j)] (out, [T, L]);
+ *   dw_down [L, D] f32 (out) = dx_lat^T x;  dx [T, D] f32 (in/out) += dx_lat . w_down            */
+lmoe_status lmoe_bwd_down(const lmoe_shape* shape, const void* x, const void* dx_perm, const int32_t* slot_of_pair,
+                          const void* w_down_t, void* dx_lat, float* dw_down, float* dx, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* B6 (A10 reversed, packed shared experts): [g_s | u_s] = x . w1s_packed^T recomputed;
+ *   dgu_shared [T, 2*S*I_s] (out) = [dg_s | du_s] of SiTU-GLU for dh_shared (B1);
+ *   dw1s_packed [2*S*I_s, D] f32 (out) = dgu_shared^T x;  dx [T, D] f32 (in/out) += dgu_shared . w1s_packed */
+lmoe_status lmoe_bwd_shared(const lmoe_shape* shape, const void* x, const void* w1s_packed, const void* w1s_t,
+                            const void* dh_shared, void* dgu_shared, float* dw1s_packed, float* dx, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* Kernel timing for measurement. When enabled, every kernel the library enqueues is bracketed by
  * HIP events on its stream. lmoe_profile_collect() synchronises those events and folds them into

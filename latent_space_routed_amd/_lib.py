@@ -17,10 +17,14 @@ LIB_PATH = os.path.join(_PKG, "liblmoe.so")
 LMOE_OK, LMOE_ERR_INVALID_ARGUMENT, LMOE_ERR_UNSUPPORTED, LMOE_ERR_WORKSPACE, LMOE_ERR_HIP = range(5)
 LMOE_F32, LMOE_BF16 = 0, 1
 LMOE_CALL_ROUTE, LMOE_CALL_PERMUTE, LMOE_CALL_GROUPED_GLU, LMOE_CALL_COMBINE_NORM_UP = 0, 1, 2, 3
+LMOE_CALL_BWD_UP, LMOE_CALL_BWD_COMBINE_NORM, LMOE_CALL_BWD_EXPERTS, LMOE_CALL_BWD_DOWN, LMOE_CALL_BWD_SHARED = \
+    16, 17, 18, 19, 20
 
 # every symbol include/lmoe.h declares
 EXPORTS = ("lmoe_workspace_bytes", "lmoe_status_string", "lmoe_route", "lmoe_qb_histogram", "lmoe_qb_update",
            "lmoe_permute", "lmoe_grouped_situ_glu", "lmoe_pack_shared", "lmoe_combine_norm_up",
+           "lmoe_bwd_transpose_weights", "lmoe_bwd_up", "lmoe_bwd_combine_norm", "lmoe_bwd_router",
+           "lmoe_bwd_experts", "lmoe_bwd_down", "lmoe_bwd_shared",
            "lmoe_profile_enable", "lmoe_profile_reset", "lmoe_profile_collect", "lmoe_profile_get")
 
 
@@ -69,6 +73,13 @@ def lib() -> ctypes.CDLL:
             "lmoe_pack_shared": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
             "lmoe_combine_norm_up": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                     _P, ctypes.c_size_t, _P]),
+            "lmoe_bwd_transpose_weights": (ctypes.c_int, [_S] + [_P] * 13),
+            "lmoe_bwd_up": (ctypes.c_int, [_S] + [_P] * 10 + [ctypes.c_size_t, _P]),
+            "lmoe_bwd_combine_norm": (ctypes.c_int, [_S] + [_P] * 12 + [ctypes.c_size_t, _P]),
+            "lmoe_bwd_router": (ctypes.c_int, [_S] + [_P] * 10),
+            "lmoe_bwd_experts": (ctypes.c_int, [_S] + [_P] * 14 + [ctypes.c_size_t, _P]),
+            "lmoe_bwd_down": (ctypes.c_int, [_S] + [_P] * 8 + [ctypes.c_size_t, _P]),
+            "lmoe_bwd_shared": (ctypes.c_int, [_S] + [_P] * 8 + [ctypes.c_size_t, _P]),
             "lmoe_profile_enable": (None, [ctypes.c_int]),
             "lmoe_profile_reset": (None, []),
             "lmoe_profile_collect": (ctypes.c_int, []),
@@ -165,6 +176,54 @@ def lmoe_combine_norm_up(shape, y_perm, slot_of_pair, topk_w, gamma, w_up, y_sha
                                       _ptr(gamma), _ptr(w_up), _ptr(y_shared), _ptr(h_shared), _ptr(w2_shared),
                                       _ptr(n_out), _ptr(out), out_dtype, _ptr(workspace), _nbytes(workspace),
                                       _stream(stream)))
+
+
+def _call(name: str, shape, *args):
+    """Calls a backward entry point: tensors and None become pointers; a (tensor, 'ws') pair becomes
+    the workspace pointer and its size."""
+    cargs = [ctypes.byref(shape)]
+    for a in args:
+        if isinstance(a, tuple):
+            cargs += [_ptr(a[0]), _nbytes(a[0])]
+        else:
+            cargs.append(_ptr(a))
+    cargs.append(_stream(None))
+    _check(name, getattr(lib(), name)(*cargs))
+
+
+def lmoe_bwd_transpose_weights(shape, w1, w2, w_up, w2s_packed, w1s_packed, w_down, w1_t, w2_t, w_up_t, w2s_t, w1s_t,
+                               w_down_t):
+    _call("lmoe_bwd_transpose_weights", shape, w1, w2, w_up, w2s_packed, w1s_packed, w_down, w1_t, w2_t, w_up_t,
+          w2s_t, w1s_t, w_down_t)
+
+
+def lmoe_bwd_up(shape, dout, n, h_shared, w_up_t, w2s_t, dn, dh_shared, dw_up, dw2_shared, workspace):
+    _call("lmoe_bwd_up", shape, dout, n, h_shared, w_up_t, w2s_t, dn, dh_shared, dw_up, dw2_shared, (workspace, "ws"))
+
+
+def lmoe_bwd_combine_norm(shape, dn, y_perm, slot_of_pair, topk_idx, scores, topk_w, gamma, dy_perm, dlogit,
+                          dlogit_sorted, dgamma, workspace):
+    _call("lmoe_bwd_combine_norm", shape, dn, y_perm, slot_of_pair, topk_idx, scores, topk_w, gamma, dy_perm, dlogit,
+          dlogit_sorted, dgamma, (workspace, "ws"))
+
+
+def lmoe_bwd_router(shape, x, w_router, dlogit, dlogit_sorted, topk_idx, expert_offsets, sorted_token, dw_router, dx):
+    _call("lmoe_bwd_router", shape, x, w_router, dlogit, dlogit_sorted, topk_idx, expert_offsets, sorted_token,
+          dw_router, dx)
+
+
+def lmoe_bwd_experts(shape, x_lat, sorted_token, expert_offsets, w1, w1_t, w2_t, h, dy_perm, dh, dgu, dx_perm, dw1,
+                     dw2, workspace):
+    _call("lmoe_bwd_experts", shape, x_lat, sorted_token, expert_offsets, w1, w1_t, w2_t, h, dy_perm, dh, dgu,
+          dx_perm, dw1, dw2, (workspace, "ws"))
+
+
+def lmoe_bwd_down(shape, x, dx_perm, slot_of_pair, w_down_t, dx_lat, dw_down, dx, workspace):
+    _call("lmoe_bwd_down", shape, x, dx_perm, slot_of_pair, w_down_t, dx_lat, dw_down, dx, (workspace, "ws"))
+
+
+def lmoe_bwd_shared(shape, x, w1s_packed, w1s_t, dh_shared, dgu_shared, dw1s_packed, dx, workspace):
+    _call("lmoe_bwd_shared", shape, x, w1s_packed, w1s_t, dh_shared, dgu_shared, dw1s_packed, dx, (workspace, "ws"))
 
 
 def profile_enable(on: bool) -> None:

@@ -101,6 +101,8 @@ hipError_t run_gemm(const GemmArgs& a, int dtype, Epi epi, GemmShape shape, cons
 
 }  // namespace
 
+lmoe_status lmoe::validate_shape(const lmoe_shape* sh) { return check_shape(sh); }
+
 extern "C" {
 
 const char* lmoe_status_string(lmoe_status s) {
@@ -121,8 +123,8 @@ size_t lmoe_workspace_bytes(const lmoe_shape* sh, int which) {
     case LMOE_CALL_PERMUTE: return permute_ws(sh) + split_bytes(down_plan(sh), sh->T, sh->d_latent);
     case LMOE_CALL_GROUPED_GLU: return glu_ws(sh->n_experts > 1 ? sh->n_experts : 1) + shared_split_bytes(sh);
     case LMOE_CALL_COMBINE_NORM_UP: return combine_split_bytes(sh);
+    default: return bwd_workspace_bytes(sh, which);
   }
-  return 0;
 }
 
 lmoe_status lmoe_route(const lmoe_shape* sh, const void* x, const float* w_router, const float* bias,

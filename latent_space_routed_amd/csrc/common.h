@@ -83,7 +83,20 @@ struct KernelTimer {
 // ------------------------------------------------------------------------------------------------
 // launchers (return hipSuccess or the launch error)
 // ------------------------------------------------------------------------------------------------
-enum class Epi : int { Store = 0, Glu = 1, Sigmoid = 2, AddF32 = 3 };
+// Store: C = acc; Glu: C = SiTU-GLU(gate acc, up acc); Sigmoid: C = sigmoid(acc + col_bias) (f32);
+// AddF32: C = acc + residual (f32); GluBwd: from the recomputed gate/up accumulators and the
+// incoming dh (aux), C[:, c] = dg and C[:, N + c] = du (the SiTU-GLU derivative).
+enum class Epi : int { Store = 0, Glu = 1, Sigmoid = 2, AddF32 = 3, GluBwd = 4 };
+
+// Derivative of h = SiTU(g) * cap(u): returns dg and du for the incoming dh, in f32 with the
+// full-precision tanhf/expf.
+__device__ inline void situ_glu_bwd(float g, float u, float dh, float beta1, float beta2, float& dg, float& du) {
+  const float t1 = tanhf(g / beta1), sg = 1.0f / (1.0f + expf(-g)), t2 = tanhf(u / beta2);
+  const float act = beta1 * t1 * sg, cap = beta2 * t2;
+  const float dact = (1.0f - t1 * t1) * sg + beta1 * t1 * sg * (1.0f - sg);
+  dg = dh * cap * dact;
+  du = dh * act * (1.0f - t2 * t2);
+}
 
 struct GemmArgs {
   const void* A;
@@ -118,6 +131,15 @@ struct GemmArgs {
   // partial product at C + s * c_split. splits <= 1: no split.
   int splits;
   int64_t c_split;
+  // GluBwd: dh [M, N] in the input type, row stride ld_aux.
+  const void* aux;
+  int64_t ld_aux;
+  // K-grouped (weight gradients): koff [G+1] device, group g contracts K in
+  // [koff[g] * koff_scale, koff[g+1] * koff_scale) of A and B (both [*, K_total]) into its own
+  // output C + g * c_gstride of M x N. Mutually exclusive with goff.
+  const int32_t* koff;
+  int koff_scale;
+  int64_t c_gstride;
 };
 
 // K-split of a dense GEMM on few rows (decode-size batches), so that its register-pipeline tiles
@@ -138,6 +160,27 @@ enum class GemmShape : int { Big = 0, Small = 1 };
 hipError_t launch_gemm(const GemmArgs& a, int in_dtype, Epi epi, GemmShape shape, hipStream_t s);
 int gemm_block_m(GemmShape shape);
 hipError_t launch_mtile_prefix(const int32_t* goff, int G, int bm, int32_t* mtile_start, hipStream_t s);
+
+// shape validation shared by the forward and backward calls (api.hip); backward workspace sizes
+lmoe_status validate_shape(const lmoe_shape* sh);
+size_t bwd_workspace_bytes(const lmoe_shape* sh, int which);
+
+// backward (backward.hip)
+hipError_t launch_transpose(const void* in, void* out, int batch, int R, int C, int64_t in_bstride,
+                            int64_t out_bstride, int esz, hipStream_t s);
+hipError_t launch_transpose_cols(const void* in, int64_t ld_in, int C, const int32_t* goff, const int32_t* ptile,
+                                 int G, int rows, const int32_t* row_map, void* out, int64_t ld_out, int Q, int esz,
+                                 hipStream_t s);
+int combine_bwd_blocks(int T);
+hipError_t launch_combine_bwd(const void* dn, const void* y, const int32_t* slot, const int32_t* idx,
+                              const float* scores, const float* w, const float* gamma, int T, int k, int E, int L,
+                              float eps, int dtype, void* dy, float* dl, float* dl_sorted, float* part,
+                              float* dgamma, hipStream_t s);
+hipError_t launch_router_bwd(const void* x, const float* w_router, const float* dl, const float* dl_sorted,
+                             const int32_t* topk_idx, const int32_t* goff, const int32_t* sorted_token, int T, int D,
+                             int E, int k, int dtype, float* dw_router, float* dx, hipStream_t s);
+hipError_t launch_unpermute(const void* src, const int32_t* slot_of_pair, int T, int k, int L, int dtype, void* out,
+                            hipStream_t s);
 
 hipError_t launch_split3(const float* w, uint16_t* out, int rows, int cols, hipStream_t s);
 hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* idx, float* w,

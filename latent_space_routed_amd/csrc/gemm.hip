@@ -126,13 +126,15 @@ __device__ inline void store_out(const GemmArgs& p, int64_t off, float v) {
 // ------------------------------------------------------------------------------------------------
 struct TileInfo {
   int g, n0, row0, rows;
+  int k0, klen;   // contraction range of the tile (elements)
+  int64_t coff;   // element offset of the tile's output block (K-grouped GEMMs)
 };
 
 template <int BM, int BNO>
 __device__ inline bool assign_tile(const GemmArgs& p, TileInfo& t) {
   const bool grouped = p.goff != nullptr;
   const int n_tiles = (int)ceil_div(p.N, BNO);
-  const int mt_total = grouped ? p.mtile_start[p.G] : (int)ceil_div(p.M, BM);
+  const int mt_total = p.koff ? p.G * (int)ceil_div(p.M, BM) : grouped ? p.mtile_start[p.G] : (int)ceil_div(p.M, BM);
   const int total = mt_total * n_tiles;
   const int per = (total + kXcds - 1) / kXcds;
   const int loc = blockIdx.x / kXcds;
@@ -141,7 +143,21 @@ __device__ inline bool assign_tile(const GemmArgs& p, TileInfo& t) {
   if (lt >= total) return false;
   int n_tile;
   t.g = 0;
-  if (grouped) {
+  t.k0 = 0;
+  t.klen = p.K;
+  t.coff = 0;
+  if (p.koff) {  // K-grouped: group-major; inside a group n-tile major, m-tile minor
+    const int MT = (int)ceil_div(p.M, BM);
+    const int tpg = MT * n_tiles;
+    t.g = lt / tpg;
+    const int r = lt - t.g * tpg;
+    n_tile = r / MT;
+    t.row0 = (r % MT) * BM;
+    t.rows = min(BM, p.M - t.row0);
+    t.k0 = p.koff[t.g] * p.koff_scale;
+    t.klen = (p.koff[t.g + 1] - p.koff[t.g]) * p.koff_scale;
+    t.coff = (int64_t)t.g * p.c_gstride;
+  } else if (grouped) {
     const int q = lt / n_tiles;
     int lo = 0, hi = p.G;  // mtile_start[lo] <= q < mtile_start[hi]
     while (hi - lo > 1) {
@@ -171,7 +187,7 @@ __device__ inline bool assign_tile(const GemmArgs& p, TileInfo& t) {
 template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, Epi EPI>
 __device__ inline void epilogue(const GemmArgs& p, const TileInfo& t, f32x16 (&acc)[WM][WN], int wm, int wn,
                                 int lane, int na) {
-  constexpr bool GLU = EPI == Epi::Glu;
+  constexpr bool GLU = EPI == Epi::Glu || EPI == Epi::GluBwd;
   constexpr int WNO = GLU ? WN / 2 : WN;
   const float inv_b1 = 1.0f / p.beta1, inv_b2 = 1.0f / p.beta2;
 #pragma unroll
@@ -187,9 +203,17 @@ __device__ inline void epilogue(const GemmArgs& p, const TileInfo& t, f32x16 (&a
         const int r = rbk * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
         if (r >= t.rows) continue;
         const int64_t grow = t.row0 + r;
-        const int64_t off = grow * p.ldc + col;
+        const int64_t off = grow * p.ldc + col + t.coff;
         if constexpr (EPI == Epi::Store) {
           store_out(p, off, acc[i][j][q]);
+        } else if constexpr (EPI == Epi::GluBwd) {
+          const int64_t ai = grow * p.ld_aux + col;
+          const float dh = sizeof(TI) == 2 ? bf16_to_f32(static_cast<const uint16_t*>(p.aux)[ai])
+                                           : static_cast<const float*>(p.aux)[ai];
+          float dg, du;
+          situ_glu_bwd(acc[i][j][q], acc[i][j + WNO][q], dh, p.beta1, p.beta2, dg, du);
+          store_out(p, off, dg);
+          store_out(p, off + p.N, du);
         } else if constexpr (EPI == Epi::Glu) {
           store_out(p, off, situ_glu<sizeof(TI) == 4>(acc[i][j][q], acc[i][j + WNO][q], p.beta1, inv_b1, p.beta2,
                                                       inv_b2));
@@ -251,7 +275,7 @@ __device__ inline void epilogue_staged(const GemmArgs& p, const TileInfo& t, f32
       const int r = ((i0 + lr / 32) * WAVES_M + wm) * 32 + (lr % 32);
       const int col = t.n0 + (j * WAVES_N + wn) * 32 + cv;
       if (r < t.rows && col < p.N)
-        *reinterpret_cast<uint4*>(static_cast<TO*>(p.C) + (int64_t)(t.row0 + r) * p.ldc + col) =
+        *reinterpret_cast<uint4*>(static_cast<TO*>(p.C) + (int64_t)(t.row0 + r) * p.ldc + col + t.coff) =
             *reinterpret_cast<const uint4*>(region + lr * ROWB + (j * 32 + cv) * (int)sizeof(TO));
     }
     __builtin_amdgcn_wave_barrier();
@@ -290,7 +314,7 @@ gemm_dma_kernel(GemmArgs p) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int BM = WAVES_M * WM * 32;
   constexpr int BNB = WAVES_N * WN * 32;  // rows of B per tile
-  constexpr bool GLU = EPI == Epi::Glu;
+  constexpr bool GLU = EPI == Epi::Glu || EPI == Epi::GluBwd;
   static_assert(!GLU || WN % 2 == 0, "GLU needs gate/up column-block pairs");
   constexpr int BNO = GLU ? BNB / 2 : BNB;
   constexpr int WNO = GLU ? WN / 2 : WN;
@@ -314,12 +338,14 @@ gemm_dma_kernel(GemmArgs p) {
 
   const int64_t a_ld = p.lda * (int64_t)sizeof(TI), b_ld = p.ldb * (int64_t)sizeof(TI);
   const int64_t a_ld2 = p.lda2 * (int64_t)sizeof(TI), b_ld2 = p.ldb2 * (int64_t)sizeof(TI);
-  const char* Bb = static_cast<const char*>(p.B) + (int64_t)t.g * p.b_gstride * (int64_t)sizeof(TI);
+  const char* Bb = static_cast<const char*>(p.B) + (int64_t)t.g * p.b_gstride * (int64_t)sizeof(TI) +
+                   (int64_t)t.k0 * (int64_t)sizeof(TI);
   const int ncols = min(BNO, p.N - t.n0);
   const bool gather = p.a_rows != nullptr;
   const bool seg2 = !GLU && p.A2 != nullptr;
   const u32x4 a_desc = gather ? make_desc(p.A, (int)(p.a_nrows * a_ld))
-                              : make_desc(static_cast<const char*>(p.A) + (int64_t)t.row0 * a_ld, (int)(t.rows * a_ld));
+                              : make_desc(static_cast<const char*>(p.A) + (int64_t)t.row0 * a_ld +
+                                              (int64_t)t.k0 * (int64_t)sizeof(TI), (int)(t.rows * a_ld));
   const u32x4 b_desc0 = make_desc(Bb + (int64_t)t.n0 * b_ld, (int)(ncols * b_ld));
   const u32x4 b_desc1 = GLU ? make_desc(Bb + (int64_t)(p.glu_up_off + t.n0) * b_ld, (int)(ncols * b_ld)) : b_desc0;
   const u32x4 a2_desc =
@@ -327,7 +353,7 @@ gemm_dma_kernel(GemmArgs p) {
   const u32x4 b2_desc =
       seg2 ? make_desc(static_cast<const char*>(p.B2) + (int64_t)t.n0 * b_ld2, (int)(ncols * b_ld2)) : b_desc0;
   const int a_wrap = p.a_kwrap * (int)sizeof(TI);
-  const int KT = p.K * (int)sizeof(TI) / KB;
+  const int KT = t.klen * (int)sizeof(TI) / KB;
   const int KT1 = p.K1 * (int)sizeof(TI) / KB;
 
   // The lane's source chunk for each DMA block of this wave (swizzled so that LDS slot s of row r
@@ -476,7 +502,7 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_reg_kernel(GemmA
   constexpr int NT = WAVES_M * WAVES_N * kWave;
   constexpr int BM = WAVES_M * WM * 32;
   constexpr int BNB = WAVES_N * WN * 32;
-  constexpr bool GLU = EPI == Epi::Glu;
+  constexpr bool GLU = EPI == Epi::Glu || EPI == Epi::GluBwd;
   static_assert(!GLU || WN % 2 == 0, "GLU needs gate/up column-block pairs");
   constexpr int BNO = GLU ? BNB / 2 : BNB;
   constexpr int WNO = GLU ? WN / 2 : WN;
@@ -498,13 +524,15 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_reg_kernel(GemmA
 
   const int64_t a_ld = p.lda * (int64_t)sizeof(TI), b_ld = p.ldb * (int64_t)sizeof(TI);
   const int64_t a_ld2 = p.lda2 * (int64_t)sizeof(TI), b_ld2 = p.ldb2 * (int64_t)sizeof(TI);
-  const char* Bb = static_cast<const char*>(p.B) + (int64_t)t.g * p.b_gstride * (int64_t)sizeof(TI);
+  const char* Bb = static_cast<const char*>(p.B) + (int64_t)t.g * p.b_gstride * (int64_t)sizeof(TI) +
+                   (int64_t)t.k0 * (int64_t)sizeof(TI);
   const int ncols = min(BNO, p.N - t.n0);
   const bool gather = p.a_rows != nullptr;
   const bool seg2 = !GLU && p.A2 != nullptr;
   const __amdgpu_buffer_rsrc_t a_rsrc =
       gather ? make_rsrc(p.A, (int)(p.a_nrows * a_ld))
-             : make_rsrc(static_cast<const char*>(p.A) + (int64_t)t.row0 * a_ld, (int)(t.rows * a_ld));
+             : make_rsrc(static_cast<const char*>(p.A) + (int64_t)t.row0 * a_ld + (int64_t)t.k0 * (int64_t)sizeof(TI),
+                         (int)(t.rows * a_ld));
   const __amdgpu_buffer_rsrc_t b_rsrc0 = make_rsrc(Bb + (int64_t)t.n0 * b_ld, (int)(ncols * b_ld));
   const __amdgpu_buffer_rsrc_t b_rsrc1 =
       GLU ? make_rsrc(Bb + (int64_t)(p.glu_up_off + t.n0) * b_ld, (int)(ncols * b_ld)) : b_rsrc0;
@@ -513,7 +541,7 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_reg_kernel(GemmA
   const __amdgpu_buffer_rsrc_t b2_rsrc =
       seg2 ? make_rsrc(static_cast<const char*>(p.B2) + (int64_t)t.n0 * b_ld2, (int)(ncols * b_ld2)) : b_rsrc0;
   const int a_wrap = p.a_kwrap * (int)sizeof(TI);
-  const int KT = p.K * (int)sizeof(TI) / 128;
+  const int KT = t.klen * (int)sizeof(TI) / 128;
   const int KT1 = p.K1 * (int)sizeof(TI) / 128;
 
   int a_voff[A_PER], b_voff[B_PER], a2_voff[A_PER], b2_voff[B_PER];
@@ -668,9 +696,11 @@ int gcd_int(int a, int b) {
 // ------------------------------------------------------------------------------------------------
 template <int BM, int BNB>
 int64_t grid_blocks(const GemmArgs& a, Epi epi) {
-  const int bno = epi == Epi::Glu ? BNB / 2 : BNB;
+  const int bno = (epi == Epi::Glu || epi == Epi::GluBwd) ? BNB / 2 : BNB;
   const int64_t n_tiles = ceil_div(a.N, bno);
-  const int64_t m_tiles = a.goff ? (int64_t)a.M / BM + a.G : ceil_div(a.M, BM);  // upper bound if grouped
+  const int64_t m_tiles = a.koff   ? (int64_t)a.G * ceil_div(a.M, BM)
+                          : a.goff ? (int64_t)a.M / BM + a.G  // upper bound if grouped
+                                   : ceil_div(a.M, BM);
   return ceil_div(m_tiles * n_tiles, kXcds) * kXcds;
 }
 
@@ -680,6 +710,7 @@ int64_t grid_blocks(const GemmArgs& a, Epi epi) {
     case Epi::Glu: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, Epi::Glu>), grid, block, 0, s, a); break;             \
     case Epi::Sigmoid: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, Epi::Sigmoid>), grid, block, 0, s, a); break;     \
     case Epi::AddF32: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, Epi::AddF32>), grid, block, 0, s, a); break;       \
+    case Epi::GluBwd: hipLaunchKernelGGL((KERNEL<__VA_ARGS__, Epi::GluBwd>), grid, block, 0, s, a); break;       \
   }
 
 constexpr int kDmaStages = 2;    // LDS stages of the DMA pipeline
@@ -768,7 +799,8 @@ hipError_t launch_gemm_split(const GemmArgs& a, int in_dtype, Epi epi, const Spl
                              hipStream_t s) {
   const bool glu = epi == Epi::Glu;
   const int n_cols = glu ? 2 * a.N : a.N;
-  if (sp.splits < 2 || a.goff || a.a_rows || (glu && a.glu_up_off != a.N)) return hipErrorInvalidValue;
+  if (sp.splits < 2 || a.goff || a.koff || a.a_rows || epi == Epi::GluBwd || (glu && a.glu_up_off != a.N))
+    return hipErrorInvalidValue;
   GemmArgs q = a;
   q.K1 = a.A2 ? a.K1 : a.K;  // end of the first K segment
   q.K = sp.chunk;

@@ -135,6 +135,77 @@ class LatentMoE:
                                    b["n"], b["out"], workspace=b["ws_combine"])
         return b
 
+    # -------------------------------------------------------------------------------------------
+    def backward(self, x: torch.Tensor, b: dict, dout: torch.Tensor) -> dict:
+        """Gradients of <dout, out> for the batch whose forward buffers are ``b`` (from forward(x)).
+
+        dout [T, D] in the activation type. Returns activation and weight gradients (weight
+        gradients, dgamma, dlogit and dx in f32; the shared experts' in their packed layout).
+        Calls, in order: transposed weights, up-projection, combine + norm + routing weights, router,
+        routed experts, un-permutation + down-projection, shared experts.
+        """
+        cfg, w, dev, dt = self.cfg, self.w, self.device, self.dt
+        T = x.shape[0]
+        E, k, L, D, I = cfg.n_experts, cfg.top_k, cfg.d_latent, cfg.d_model, cfg.inter
+        S, Is = cfg.n_shared, cfg.inter_shared
+        Ss = S * Is
+        shape = C.make_shape(cfg, T)
+        f32 = torch.float32
+        if getattr(self, "_wt", None) is None:
+            self._wt = {
+                "w1_t": torch.empty(E, L, 2 * I, dtype=dt, device=dev),
+                "w2_t": torch.empty(E, I, L, dtype=dt, device=dev),
+                "w_up_t": torch.empty(L, D, dtype=dt, device=dev),
+                "w_down_t": torch.empty(D, L, dtype=dt, device=dev),
+                "w2s_t": torch.empty(max(Ss, 1), D, dtype=dt, device=dev),
+                "w1s_t": torch.empty(D, max(2 * Ss, 1), dtype=dt, device=dev),
+            }
+        wt = self._wt
+        shared = S > 0
+        C.lmoe_bwd_transpose_weights(shape, w["w1"], w["w2"], w["w_up"], self.w2s_packed if shared else None,
+                                     self.w1s_packed if shared else None, w["w_down"], wt["w1_t"], wt["w2_t"],
+                                     wt["w_up_t"], wt["w2s_t"] if shared else None,
+                                     wt["w1s_t"] if shared else None, wt["w_down_t"])
+        ws = {name: torch.empty(max(C.workspace_bytes(shape, which), 256), dtype=torch.uint8, device=dev)
+              for name, which in (("up", C.LMOE_CALL_BWD_UP), ("comb", C.LMOE_CALL_BWD_COMBINE_NORM),
+                                  ("exp", C.LMOE_CALL_BWD_EXPERTS), ("down", C.LMOE_CALL_BWD_DOWN),
+                                  ("sh", C.LMOE_CALL_BWD_SHARED))}
+        g = {
+            "dn": torch.empty(T, L, dtype=dt, device=dev),
+            "dh_s": torch.empty(T, max(Ss, 64), dtype=dt, device=dev),
+            "dW_up": torch.empty(D, L, dtype=f32, device=dev),
+            "dW2s_packed": torch.empty(D, max(Ss, 1), dtype=f32, device=dev),
+            "dy": torch.empty(T * k, L, dtype=dt, device=dev),
+            "dl": torch.empty(T, k, dtype=f32, device=dev),
+            "dl_sorted": torch.empty(T * k, dtype=f32, device=dev),
+            "dgamma": torch.empty(L, dtype=f32, device=dev),
+            "dW_r": torch.empty(E, D, dtype=f32, device=dev),
+            "dx": torch.empty(T, D, dtype=f32, device=dev),
+            "dh": torch.empty(T * k, I, dtype=dt, device=dev),
+            "dgu": torch.empty(T * k, 2 * I, dtype=dt, device=dev),
+            "dx_perm": torch.empty(T * k, L, dtype=dt, device=dev),
+            "dW1": torch.empty(E, 2 * I, L, dtype=f32, device=dev),
+            "dW2": torch.empty(E, L, I, dtype=f32, device=dev),
+            "dx_lat": torch.empty(T, L, dtype=dt, device=dev),
+            "dW_dn": torch.empty(L, D, dtype=f32, device=dev),
+            "dgu_s": torch.empty(T, max(2 * Ss, 64), dtype=dt, device=dev),
+            "dW1s_packed": torch.empty(max(2 * Ss, 1), D, dtype=f32, device=dev),
+        }
+        C.lmoe_bwd_up(shape, dout, b["n"], b["h_s"] if shared else None, wt["w_up_t"], wt["w2s_t"] if shared else None,
+                      g["dn"], g["dh_s"] if shared else None, g["dW_up"], g["dW2s_packed"] if shared else None, ws["up"])
+        C.lmoe_bwd_combine_norm(shape, g["dn"], b["y"], b["slot_of_pair"], b["idx"], b["scores"], b["w"],
+                                w.get("gamma"), g["dy"], g["dl"], g["dl_sorted"], g["dgamma"], ws["comb"])
+        C.lmoe_bwd_router(shape, x, w["w_router"], g["dl"], g["dl_sorted"], b["idx"], b["offsets"], b["sorted_token"],
+                          g["dW_r"], g["dx"])
+        C.lmoe_bwd_experts(shape, b["x_lat"], b["sorted_token"], b["offsets"], w["w1"], wt["w1_t"], wt["w2_t"], b["h"],
+                           g["dy"], g["dh"], g["dgu"], g["dx_perm"], g["dW1"], g["dW2"], ws["exp"])
+        C.lmoe_bwd_down(shape, x, g["dx_perm"], b["slot_of_pair"], wt["w_down_t"], g["dx_lat"], g["dW_dn"], g["dx"],
+                        ws["down"])
+        if shared:
+            C.lmoe_bwd_shared(shape, x, self.w1s_packed, wt["w1s_t"], g["dh_s"], g["dgu_s"], g["dW1s_packed"], g["dx"],
+                              ws["sh"])
+        return g
+
     def qb_update(self) -> None:
         """Move the selection bias from the accumulated histogram and reset it (a step boundary)."""
         C.lmoe_qb_update(C.make_shape(self.cfg, 0), self.hist, self.n_acc, self.bias)
