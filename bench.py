@@ -132,6 +132,44 @@ def cpu_baseline(cfg, inp, sample_tokens: int) -> dict:
                       f"{dt:.1f} s"}
 
 
+BWD_KERNELS = ["bwd_transpose", "bwd_gemm_dn", "bwd_gemm_dw", "bwd_combine_norm", "bwd_dgamma", "bwd_router_dw",
+               "bwd_router_dx", "bwd_gemm_dh", "bwd_gemm_dw_experts", "bwd_gemm_dgu", "bwd_gemm_dx_experts",
+               "bwd_unpermute", "bwd_gemm_dx"]
+
+
+def train_steps(layer, x, cfg, args, _lib, torch) -> dict:
+    """Training steps: forward, backward of <dout, out> for a fixed synthetic dout, bias update."""
+    g = torch.Generator(device="cuda").manual_seed(7)
+    dout = torch.randn(cfg.T, cfg.d_model, device="cuda", generator=g).to(layer.dt)
+
+    def step():
+        b = layer.forward(x)
+        layer.backward(x, b, dout)
+        layer.qb_update()
+
+    log("[bench] training-step warmup")
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    _lib.profile_reset()
+    _lib.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    _lib.profile_enable(False)
+    _lib.profile_collect()
+    kernels = {}
+    for n in BWD_KERNELS:
+        cnt, ms = _lib.profile_get(n)
+        if cnt:
+            kernels[n] = round(ms / args.steps, 4)
+    ms_step = elapsed / args.steps * 1e3
+    return {"ms_per_step": ms_step, "tokens_per_s": cfg.T / (ms_step / 1e3),
+            "backward_kernels_ms_per_step": kernels, "backward_kernels_sum_ms": round(sum(kernels.values()), 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +178,8 @@ def main() -> int:
     ap.add_argument("--workload", default="k3_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=256)
+    ap.add_argument("--backward", action="store_true",
+                    help="also time training steps (forward + backward + bias update) and report them under 'train'")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB 5 times (counter calibration)")
     args = ap.parse_args()
@@ -252,6 +292,8 @@ def main() -> int:
         "kernels_ms_per_step": kernels,
         "kernels_roofline": kernel_roofline(kernel_work(cfg, offsets, layer.fused), kernels),
     }
+    if args.backward:
+        out["train"] = train_steps(layer, x, cfg, args, _lib, torch)
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on {args.cpu_sample} tokens")
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)

@@ -35,8 +35,9 @@ int64_t shared_inner(const lmoe_shape* sh) { return (int64_t)sh->n_shared * sh->
 size_t ws_up(const lmoe_shape* sh) {
   return round_up((size_t)(sh->d_model + sh->d_latent + shared_inner(sh)) * tpad(sh) * esize(sh->act_dtype));
 }
-size_t ws_combine(const lmoe_shape* sh) {
-  return round_up((size_t)combine_bwd_blocks(sh->T) * sh->d_latent * sizeof(float));
+size_t ws_combine(const lmoe_shape* sh) {  // block partials of dgamma and their first fold
+  const size_t blocks = (size_t)combine_bwd_blocks(sh->T);
+  return round_up((blocks + (blocks + 63) / 64) * sh->d_latent * sizeof(float));
 }
 size_t ws_experts(const lmoe_shape* sh) {
   const size_t idx = 2 * round_up((size_t)(sh->n_experts + 1) * 4);

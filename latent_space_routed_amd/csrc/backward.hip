@@ -11,27 +11,49 @@ namespace lmoe {
 namespace {
 
 // ------------------------------------------------------------------------------------------------
-// transposes (64 x 64 tiles through LDS)
+// transposes: 64 x 64 tiles through LDS, 16-byte loads along the input rows and 16-byte stores
+// along the output rows (V = 16 / sizeof(T) elements per access)
 // ------------------------------------------------------------------------------------------------
-// out[b][c][r] = in[b][r][c] for in [B][R][C] row-major.
+template <typename T>
+struct Pack16 {
+  static constexpr int V = 16 / (int)sizeof(T);
+};
+
+template <typename T>
+__device__ inline void tile_to_out(const T (*tile)[64 + 16 / sizeof(T)], T* __restrict__ out, int64_t ld_out,
+                                   int c0, int q0, int C, int Q) {
+  constexpr int V = Pack16<T>::V;
+  constexpr int SEGS = 64 / V;  // 16-byte chunks per output row of the tile
+  for (int ch = threadIdx.x; ch < 64 * SEGS; ch += 256) {
+    const int oc = ch / SEGS, seg = ch % SEGS;
+    const int c = c0 + oc, q = q0 + seg * V;
+    if (c >= C || q >= Q) continue;
+    T v[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) v[i] = tile[seg * V + i][oc];
+    *reinterpret_cast<uint4*>(out + (int64_t)c * ld_out + q) = *reinterpret_cast<const uint4*>(v);
+  }
+}
+
+// out[b][c][r] = in[b][r][c] for in [B][R][C] row-major; R and C multiples of 16 / sizeof(T).
 template <typename T>
 __global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ in, T* __restrict__ out, int R, int C,
                                                         int64_t in_bstride, int64_t out_bstride) {
-  __shared__ T tile[64][65];
+  constexpr int V = Pack16<T>::V;
+  constexpr int SEGS = 64 / V;
+  __shared__ __attribute__((aligned(16))) T tile[64][64 + V];
   const int64_t b = blockIdx.z;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const T* src = in + b * in_bstride;
-  T* dst = out + b * out_bstride;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    if (r < R && c < C) tile[i][tx] = src[(int64_t)r * C + c];
+  for (int ch = threadIdx.x; ch < 64 * SEGS; ch += 256) {
+    const int i = ch / SEGS, seg = ch % SEGS;
+    const int r = r0 + i, c = c0 + seg * V;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < R && c < C) v = *reinterpret_cast<const uint4*>(src + (int64_t)r * C + c);
+    *reinterpret_cast<uint4*>(&tile[i][seg * V]) = v;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < C && r < R) dst[(int64_t)c * R + r] = tile[tx][i];
-  }
+  tile_to_out<T>(tile, out + b * out_bstride, R, c0, r0, C, R);
 }
 
 // out[c][q] (ld_out columns) for q in [0, Q): column q takes input row src(q), or zero.
@@ -39,17 +61,19 @@ __global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ in
 //     n_g = goff[g+1] - goff[g], and the rest of the group's 64-padded range is zero; ptile is the
 //     prefix of ceil(n_g / 64);
 //   plain: column q < rows takes row q, the rest is zero.
-// With row_map the source row r is read at in[row_map[r]] (a gather).
+// With row_map the source row r is read at in[row_map[r]] (a gather). C and Q are multiples of
+// 16 / sizeof(T).
 template <typename T>
 __global__ void __launch_bounds__(256) transpose_cols_kernel(const T* __restrict__ in, int64_t ld_in, int C,
                                                              const int32_t* __restrict__ goff,
                                                              const int32_t* __restrict__ ptile, int G, int rows,
                                                              const int32_t* __restrict__ row_map, T* __restrict__ out,
                                                              int64_t ld_out, int Q) {
-  __shared__ T tile[64][65];
+  constexpr int V = Pack16<T>::V;
+  constexpr int SEGS = 64 / V;
+  __shared__ __attribute__((aligned(16))) T tile[64][64 + V];
   __shared__ int src[64];
   const int q0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   if (threadIdx.x < 64) {
     const int q = q0 + threadIdx.x;
     int sr = -1;
@@ -72,17 +96,15 @@ __global__ void __launch_bounds__(256) transpose_cols_kernel(const T* __restrict
     src[threadIdx.x] = sr;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int sr = src[i], c = c0 + tx;
-    T v = T(0);
-    if (sr >= 0 && c < C) v = in[(int64_t)sr * ld_in + c];
-    tile[i][tx] = v;
+  for (int ch = threadIdx.x; ch < 64 * SEGS; ch += 256) {
+    const int i = ch / SEGS, seg = ch % SEGS;
+    const int sr = src[i], c = c0 + seg * V;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (sr >= 0 && c < C) v = *reinterpret_cast<const uint4*>(in + (int64_t)sr * ld_in + c);
+    *reinterpret_cast<uint4*>(&tile[i][seg * V]) = v;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, q = q0 + tx;
-    if (c < C && q < Q) out[(int64_t)c * ld_out + q] = tile[tx][i];
-  }
+  tile_to_out<T>(tile, out, ld_out, c0, q0, C, Q);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -131,7 +153,7 @@ __device__ inline float wave_sum(float v) {
 // ------------------------------------------------------------------------------------------------
 // combine + RMSNorm + routing-weight backward: one wave per token, kTokPerWave tokens per wave
 // ------------------------------------------------------------------------------------------------
-constexpr int kTokPerWave = 8;
+constexpr int kTokPerWave = 1;
 constexpr int kTokPerBlock = 4 * kTokPerWave;
 
 // Per token t (lane owns chunks c = lane + 64 i of the latent row):
@@ -282,13 +304,16 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(const T* __restrict__ 
   }
 }
 
+// out[g][l] = sum over rows b in [64 g, 64 g + 64) of part[b][l], in row order.
 __global__ void __launch_bounds__(256) sum_rows_kernel(const float* __restrict__ part, int nrows, int L,
                                                        float* __restrict__ out) {
   const int l = blockIdx.x * 256 + threadIdx.x;
+  const int g = blockIdx.y;
   if (l >= L) return;
+  const int b1 = min(nrows, 64 * (g + 1));
   float a = 0.0f;
-  for (int b = 0; b < nrows; ++b) a += part[(int64_t)b * L + l];
-  out[l] = a;
+  for (int b = 64 * g; b < b1; ++b) a += part[(int64_t)b * L + l];
+  out[(int64_t)g * L + l] = a;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -451,9 +476,21 @@ hipError_t launch_combine_bwd(const void* dn, const void* y, const int32_t* slot
             : combine_bwd_t<float>(dn, y, slot, idx, scores, w, gamma, T, k, E, L, eps, dy, dl, dl_sorted, part, s);
     if (e != hipSuccess) return e;
   }
+  // dgamma = sum of the block partials, folding 64 rows at a time in row order; the levels alternate
+  // between the partial rows and the region after them (part holds blocks + ceil(blocks / 64) rows)
   KernelTimer timer("bwd_dgamma", s);
-  hipLaunchKernelGGL(sum_rows_kernel, dim3((unsigned)ceil_div(L, 256)), dim3(256), 0, s, part, combine_bwd_blocks(T), L,
-                     dgamma);
+  const int blocks = combine_bwd_blocks(T);
+  float* bufs[2] = {part, part + (size_t)blocks * L};
+  int cur = 0, nrows = blocks;
+  for (;;) {
+    const int groups = (int)ceil_div(nrows, 64);
+    float* dst = groups == 1 ? dgamma : bufs[cur ^ 1];
+    hipLaunchKernelGGL(sum_rows_kernel, dim3((unsigned)ceil_div(L, 256), (unsigned)groups), dim3(256), 0, s, bufs[cur],
+                       nrows, L, dst);
+    if (groups == 1) break;
+    nrows = groups;
+    cur ^= 1;
+  }
   return hipGetLastError();
 }
 
