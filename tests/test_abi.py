@@ -115,3 +115,22 @@ def test_empty_batch_is_a_no_op(lib):
     assert lib.lmoe_qb_histogram(ctypes.byref(sh), null, null, null, null, null, null) == C.LMOE_OK
     assert lib.lmoe_combine_norm_up(ctypes.byref(sh), null, null, null, null, null, null, null, null, null, null, 0,
                                     null, 0, null) == C.LMOE_OK
+
+
+def test_backward_workspace_and_validation(lib):
+    """Backward calls: workspace sizes for every call id, argument checks before any launch."""
+    k3 = C.make_shape(CONFIGS["k3_prefill"])
+    for which in (C.LMOE_CALL_BWD_UP, C.LMOE_CALL_BWD_COMBINE_NORM, C.LMOE_CALL_BWD_EXPERTS, C.LMOE_CALL_BWD_DOWN,
+                  C.LMOE_CALL_BWD_SHARED):
+        assert C.workspace_bytes(k3, which) > 0
+    # experts: two 1-int prefixes, then [L + I + 2I + L] x (T*k + 64 E) transposed activations
+    kp = 8192 * 16 + 64 * 896
+    assert C.workspace_bytes(k3, C.LMOE_CALL_BWD_EXPERTS) == 2 * 3840 + (3584 * 2 + 3 * 512) * kp * 2
+    big = C.make_shape(CONFIGS["k3_prefill"])
+    big.d_latent = 4096 + 64                                   # past the combine backward row limit (bf16)
+    null = None
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.lmoe_bwd_router(ctypes.byref(big), *([fake] * 9), null) == C.LMOE_ERR_UNSUPPORTED
+    assert lib.lmoe_bwd_router(ctypes.byref(k3), fake, fake, fake, fake, fake, fake, fake, fake, null, null) == \
+        C.LMOE_ERR_INVALID_ARGUMENT
+    assert lib.lmoe_bwd_up(ctypes.byref(k3), *([fake] * 9), null, 0, null) == C.LMOE_ERR_WORKSPACE
