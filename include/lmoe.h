@@ -196,15 +196,15 @@ lmoe_status lmoe_combine_norm_up(const lmoe_shape* shape, const void* y_perm, co
  * Workspace: lmoe_workspace_bytes(shape, LMOE_CALL_BWD_*); transposed activations live there.
  * ============================================================================================== */
 
-/* B0: transposed weight copies (the backward contracts over the forward's output dimension).
- * Re-run after every weight change.
- *   w1 [E, 2I, L] -> w1_t [E, L, 2I];  w2 [E, L, I] -> w2_t [E, I, L];  w_up [D, L] -> w_up_t [L, D];
- *   w_down [L, D] -> w_down_t [D, L];  w2s_packed [D, S*I_s] -> w2s_t [S*I_s, D];
- *   w1s_packed [2*S*I_s, D] -> w1s_t [D, 2*S*I_s]  (the shared pair may both be NULL)           */
-lmoe_status lmoe_bwd_transpose_weights(const lmoe_shape* shape, const void* w1, const void* w2, const void* w_up,
-                                       const void* w2s_packed, const void* w1s_packed, const void* w_down,
-                                       void* w1_t, void* w2_t, void* w_up_t, void* w2s_t, void* w1s_t,
-                                       void* w_down_t, void* stream);
+/* B0: transposed copies of the dense weights (their backward products contract over the forward's
+ * output dimension and run on the 256x256 MFMA pipeline). Re-run after every weight change. The
+ * routed experts' weights need no copy: their products read them in place.
+ *   w_up [D, L] -> w_up_t [L, D];  w_down [L, D] -> w_down_t [D, L];
+ *   w2s_packed [D, S*I_s] -> w2s_t [S*I_s, D];  w1s_packed [2*S*I_s, D] -> w1s_t [D, 2*S*I_s]
+ *   (the shared pair may both be NULL)                                                           */
+lmoe_status lmoe_bwd_transpose_weights(const lmoe_shape* shape, const void* w_up, const void* w2s_packed,
+                                       const void* w1s_packed, const void* w_down, void* w_up_t, void* w2s_t,
+                                       void* w1s_t, void* w_down_t, void* stream);
 
 /* B1 (A11 reversed): out = [n | h_s] . [w_up | w2s_packed]^T.
  *   dout [T, D], n [T, L], h_shared [T, S*I_s] or NULL (then no shared part), w_up_t, w2s_t from B0
@@ -237,11 +237,12 @@ lmoe_status lmoe_bwd_router(const lmoe_shape* shape, const void* x, const float*
  *   dh = dy . w2_e (out, [T*k, I]);  dw2_e = dy_e^T h_e (f32 [E, L, I], out)
  *   [g | u] = x_lat[sorted_token] . w1_e^T recomputed; dgu (out, [T*k, 2I]) = [dg | du] of SiTU-GLU
  *   dx_perm = dgu . w1_e (out, [T*k, L]);  dw1_e = dgu_e^T x_lat[sorted_token]_e (f32 [E, 2I, L], out)
- *   x_lat [T, L], sorted_token, expert_offsets, w1, h [T*k, I], dy_perm: forward tensors / B2; w1_t, w2_t: B0 */
+ *   x_lat [T, L], sorted_token, expert_offsets, w1 [E, 2I, L], w2 [E, L, I], h [T*k, I], dy_perm:
+ *   forward tensors and weights / B2                                                              */
 lmoe_status lmoe_bwd_experts(const lmoe_shape* shape, const void* x_lat, const int32_t* sorted_token,
-                             const int32_t* expert_offsets, const void* w1, const void* w1_t, const void* w2_t,
-                             const void* h, const void* dy_perm, void* dh, void* dgu, void* dx_perm, float* dw1,
-                             float* dw2, void* workspace, size_t workspace_bytes, void* stream);
+                             const int32_t* expert_offsets, const void* w1, const void* w2, const void* h,
+                             const void* dy_perm, void* dh, void* dgu, void* dx_perm, float* dw1, float* dw2,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* B5 (A6 + A5 reversed): dx_lat[t] = sum_j dx_perm[slot(t,j)] (out, [T, L]);
  *   dw_down [L, D] f32 (out) = dx_lat^T x;  dx [T, D] f32 (in/out) += dx_lat . w_down            */

@@ -73,11 +73,11 @@ def lib() -> ctypes.CDLL:
             "lmoe_pack_shared": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
             "lmoe_combine_norm_up": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                     _P, ctypes.c_size_t, _P]),
-            "lmoe_bwd_transpose_weights": (ctypes.c_int, [_S] + [_P] * 13),
+            "lmoe_bwd_transpose_weights": (ctypes.c_int, [_S] + [_P] * 9),
             "lmoe_bwd_up": (ctypes.c_int, [_S] + [_P] * 10 + [ctypes.c_size_t, _P]),
             "lmoe_bwd_combine_norm": (ctypes.c_int, [_S] + [_P] * 12 + [ctypes.c_size_t, _P]),
             "lmoe_bwd_router": (ctypes.c_int, [_S] + [_P] * 10),
-            "lmoe_bwd_experts": (ctypes.c_int, [_S] + [_P] * 14 + [ctypes.c_size_t, _P]),
+            "lmoe_bwd_experts": (ctypes.c_int, [_S] + [_P] * 13 + [ctypes.c_size_t, _P]),
             "lmoe_bwd_down": (ctypes.c_int, [_S] + [_P] * 8 + [ctypes.c_size_t, _P]),
             "lmoe_bwd_shared": (ctypes.c_int, [_S] + [_P] * 8 + [ctypes.c_size_t, _P]),
             "lmoe_profile_enable": (None, [ctypes.c_int]),
@@ -191,10 +191,8 @@ def _call(name: str, shape, *args):
     _check(name, getattr(lib(), name)(*cargs))
 
 
-def lmoe_bwd_transpose_weights(shape, w1, w2, w_up, w2s_packed, w1s_packed, w_down, w1_t, w2_t, w_up_t, w2s_t, w1s_t,
-                               w_down_t):
-    _call("lmoe_bwd_transpose_weights", shape, w1, w2, w_up, w2s_packed, w1s_packed, w_down, w1_t, w2_t, w_up_t,
-          w2s_t, w1s_t, w_down_t)
+def lmoe_bwd_transpose_weights(shape, w_up, w2s_packed, w1s_packed, w_down, w_up_t, w2s_t, w1s_t, w_down_t):
+    _call("lmoe_bwd_transpose_weights", shape, w_up, w2s_packed, w1s_packed, w_down, w_up_t, w2s_t, w1s_t, w_down_t)
 
 
 def lmoe_bwd_up(shape, dout, n, h_shared, w_up_t, w2s_t, dn, dh_shared, dw_up, dw2_shared, workspace):
@@ -212,10 +210,10 @@ def lmoe_bwd_router(shape, x, w_router, dlogit, dlogit_sorted, topk_idx, expert_
           dw_router, dx)
 
 
-def lmoe_bwd_experts(shape, x_lat, sorted_token, expert_offsets, w1, w1_t, w2_t, h, dy_perm, dh, dgu, dx_perm, dw1,
-                     dw2, workspace):
-    _call("lmoe_bwd_experts", shape, x_lat, sorted_token, expert_offsets, w1, w1_t, w2_t, h, dy_perm, dh, dgu,
-          dx_perm, dw1, dw2, (workspace, "ws"))
+def lmoe_bwd_experts(shape, x_lat, sorted_token, expert_offsets, w1, w2, h, dy_perm, dh, dgu, dx_perm, dw1, dw2,
+                     workspace):
+    _call("lmoe_bwd_experts", shape, x_lat, sorted_token, expert_offsets, w1, w2, h, dy_perm, dh, dgu, dx_perm, dw1,
+          dw2, (workspace, "ws"))
 
 
 def lmoe_bwd_down(shape, x, dx_perm, slot_of_pair, w_down_t, dx_lat, dw_down, dx, workspace):

@@ -40,7 +40,7 @@ size_t ws_combine(const lmoe_shape* sh) {  // block partials of dgamma and their
   return round_up((blocks + (blocks + 63) / 64) * sh->d_latent * sizeof(float));
 }
 size_t ws_experts(const lmoe_shape* sh) {
-  const size_t idx = 2 * round_up((size_t)(sh->n_experts + 1) * 4);
+  const size_t idx = 3 * round_up((size_t)(sh->n_experts + 1) * 4);
   const size_t rows = (size_t)(sh->d_latent + sh->inter + 2 * sh->inter + sh->d_latent);
   return idx + round_up(rows * kpad(sh) * esize(sh->act_dtype));
 }
@@ -110,14 +110,12 @@ size_t bwd_workspace_bytes(const lmoe_shape* sh, int which) {
 
 extern "C" {
 
-lmoe_status lmoe_bwd_transpose_weights(const lmoe_shape* sh, const void* w1, const void* w2, const void* w_up,
-                                       const void* w2s_packed, const void* w1s_packed, const void* w_down, void* w1_t,
-                                       void* w2_t, void* w_up_t, void* w2s_t, void* w1s_t, void* w_down_t,
-                                       void* stream) {
+lmoe_status lmoe_bwd_transpose_weights(const lmoe_shape* sh, const void* w_up, const void* w2s_packed,
+                                       const void* w1s_packed, const void* w_down, void* w_up_t, void* w2s_t,
+                                       void* w1s_t, void* w_down_t, void* stream) {
   lmoe_status st = check_bwd_shape(sh);
   if (st != LMOE_OK) return st;
-  if (!aligned16(w1) || !aligned16(w2) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(w1_t) ||
-      !aligned16(w2_t) || !aligned16(w_up_t) || !aligned16(w_down_t))
+  if (!aligned16(w_up) || !aligned16(w_down) || !aligned16(w_up_t) || !aligned16(w_down_t))
     return LMOE_ERR_INVALID_ARGUMENT;
   const int64_t Ss = shared_inner(sh);
   const bool shared = w2s_packed || w1s_packed;
@@ -125,10 +123,8 @@ lmoe_status lmoe_bwd_transpose_weights(const lmoe_shape* sh, const void* w1, con
                  !aligned16(w1s_t)))
     return LMOE_ERR_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int E = sh->n_experts, D = sh->d_model, L = sh->d_latent, I = sh->inter, esz = esize(sh->act_dtype);
-  st = hip_status(launch_transpose(w1, w1_t, E, 2 * I, L, (int64_t)2 * I * L, (int64_t)2 * I * L, esz, s));
-  if (st == LMOE_OK) st = hip_status(launch_transpose(w2, w2_t, E, L, I, (int64_t)L * I, (int64_t)L * I, esz, s));
-  if (st == LMOE_OK) st = hip_status(launch_transpose(w_up, w_up_t, 1, D, L, 0, 0, esz, s));
+  const int D = sh->d_model, L = sh->d_latent, esz = esize(sh->act_dtype);
+  st = hip_status(launch_transpose(w_up, w_up_t, 1, D, L, 0, 0, esz, s));
   if (st == LMOE_OK) st = hip_status(launch_transpose(w_down, w_down_t, 1, L, D, 0, 0, esz, s));
   if (st == LMOE_OK && shared) st = hip_status(launch_transpose(w2s_packed, w2s_t, 1, D, (int)Ss, 0, 0, esz, s));
   if (st == LMOE_OK && shared) st = hip_status(launch_transpose(w1s_packed, w1s_t, 1, (int)(2 * Ss), D, 0, 0, esz, s));
@@ -204,13 +200,13 @@ lmoe_status lmoe_bwd_router(const lmoe_shape* sh, const void* x, const float* w_
 }
 
 lmoe_status lmoe_bwd_experts(const lmoe_shape* sh, const void* x_lat, const int32_t* sorted_token,
-                             const int32_t* expert_offsets, const void* w1, const void* w1_t, const void* w2_t,
-                             const void* h, const void* dy_perm, void* dh, void* dgu, void* dx_perm, float* dw1,
-                             float* dw2, void* workspace, size_t workspace_bytes, void* stream) {
+                             const int32_t* expert_offsets, const void* w1, const void* w2, const void* h,
+                             const void* dy_perm, void* dh, void* dgu, void* dx_perm, float* dw1, float* dw2,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   lmoe_status st = check_bwd_shape(sh);
   if (st != LMOE_OK) return st;
   if (!aligned16(x_lat) || !aligned4(sorted_token) || !aligned4(expert_offsets) || !aligned16(w1) ||
-      !aligned16(w1_t) || !aligned16(w2_t) || !aligned16(h) || !aligned16(dy_perm) || !aligned16(dh) ||
+      !aligned16(w2) || !aligned16(h) || !aligned16(dy_perm) || !aligned16(dh) ||
       !aligned16(dgu) || !aligned16(dx_perm) || !aligned16(dw1) || !aligned16(dw2))
     return LMOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(workspace) || workspace_bytes < ws_experts(sh)) return LMOE_ERR_WORKSPACE;
@@ -220,9 +216,11 @@ lmoe_status lmoe_bwd_experts(const lmoe_shape* sh, const void* x_lat, const int3
   const int rows = T * sh->top_k;
   const int64_t Kp = kpad(sh);
   char* ws = static_cast<char*>(workspace);
-  int32_t* mts = reinterpret_cast<int32_t*>(ws);                                    // grouped m-tile prefix
-  int32_t* ptile = reinterpret_cast<int32_t*>(ws + round_up((size_t)(E + 1) * 4));  // 64-row tile prefix
-  char* tb = ws + 2 * round_up((size_t)(E + 1) * 4);
+  const size_t ia = round_up((size_t)(E + 1) * 4);
+  int32_t* mts = reinterpret_cast<int32_t*>(ws);                // m-tile prefix of the recomputed GEMM1
+  int32_t* mts128 = reinterpret_cast<int32_t*>(ws + ia);        // 128-row m-tile prefix ([K, N] weights)
+  int32_t* ptile = reinterpret_cast<int32_t*>(ws + 2 * ia);     // 64-row tile prefix (padded K ranges)
+  char* tb = ws + 3 * ia;
   void* dy_t = tb;                                       // [L, Kp]
   void* h_t = tb + (size_t)L * Kp * esz;                 // [I, Kp]
   void* dgu_t = tb + (size_t)(L + I) * Kp * esz;         // [2I, Kp]
@@ -230,6 +228,7 @@ lmoe_status lmoe_bwd_experts(const lmoe_shape* sh, const void* x_lat, const int3
   // with no rows every K-range is empty and the K-grouped GEMMs write zero gradients
   const GemmShape gshape = (int64_t)rows >= (int64_t)E * 64 ? GemmShape::Big : GemmShape::Small;
   st = hip_status(launch_mtile_prefix(expert_offsets, E, gemm_block_m(gshape), mts, s));
+  if (st == LMOE_OK) st = hip_status(launch_mtile_prefix(expert_offsets, E, 128, mts128, s));
   if (st == LMOE_OK) st = hip_status(launch_mtile_prefix(expert_offsets, E, 64, ptile, s));
   if (st != LMOE_OK) return st;
   auto grouped = [&](const void* A, int64_t lda, const void* B, int64_t ldb, int64_t bstride, void* C, int64_t ldc,
@@ -273,10 +272,12 @@ lmoe_status lmoe_bwd_experts(const lmoe_shape* sh, const void* x_lat, const int3
     a.tag = tag;
     return launch_gemm(a, dt, Epi::Store, (int64_t)M * N >= 256 * 256 ? GemmShape::Big : GemmShape::Small, s);
   };
-  // dh = dy . W2_e
+  // dh = dy . W2_e, W2_e read as [K = L, N = I]
   if (rows > 0) {
-    GemmArgs a = grouped(dy_perm, L, w2_t, L, (int64_t)I * L, dh, I, I, L, "bwd_gemm_dh");
-    st = hip_status(launch_gemm(a, dt, Epi::Store, gshape, s));
+    GemmArgs a = grouped(dy_perm, L, w2, I, (int64_t)L * I, dh, I, I, L, "bwd_gemm_dh");
+    a.mtile_start = mts128;
+    a.b_kn = true;
+    st = hip_status(launch_gemm(a, dt, Epi::Store, GemmShape::Small, s));
   }
   // dW2_e = dy_e^T h_e
   if (st == LMOE_OK)
@@ -296,10 +297,12 @@ lmoe_status lmoe_bwd_experts(const lmoe_shape* sh, const void* x_lat, const int3
     a.ld_aux = I;
     st = hip_status(launch_gemm(a, dt, Epi::GluBwd, gshape, s));
   }
-  // dx_perm = d[g | u] . W1_e
+  // dx_perm = d[g | u] . W1_e, W1_e read as [K = 2I, N = L]
   if (st == LMOE_OK && rows > 0) {
-    GemmArgs a = grouped(dgu, 2 * I, w1_t, 2 * I, (int64_t)L * 2 * I, dx_perm, L, L, 2 * I, "bwd_gemm_dx_experts");
-    st = hip_status(launch_gemm(a, dt, Epi::Store, gshape, s));
+    GemmArgs a = grouped(dgu, 2 * I, w1, L, (int64_t)2 * I * L, dx_perm, L, L, 2 * I, "bwd_gemm_dx_experts");
+    a.mtile_start = mts128;
+    a.b_kn = true;
+    st = hip_status(launch_gemm(a, dt, Epi::Store, GemmShape::Small, s));
   }
   // dW1_e = d[g | u]_e^T x_perm_e (x_perm gathered from x_lat through sorted_token)
   if (st == LMOE_OK)

@@ -140,6 +140,10 @@ struct GemmArgs {
   const int32_t* koff;
   int koff_scale;
   int64_t c_gstride;
+  // B stored [K, N] (row k holds every output column; ldb = row stride) instead of [N, K]: the
+  // register pipeline transposes it on its way into LDS. Store / AddF32 epilogues, no second K
+  // segment, no split.
+  bool b_kn;
 };
 
 // K-split of a dense GEMM on few rows (decode-size batches), so that its register-pipeline tiles

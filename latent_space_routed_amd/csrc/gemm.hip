@@ -545,6 +545,17 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_reg_kernel(GemmA
   const int KT1 = p.K1 * (int)sizeof(TI) / 128;
 
   int a_voff[A_PER], b_voff[B_PER], a2_voff[A_PER], b2_voff[B_PER];
+  // B stored [K, N]: each thread loads pairs of rows (2 kap, 2 kap + 1) of one 16-byte column chunk
+  // nc and writes them transposed into the [n][k] LDS layout, two k per 32-bit word (bf16) or as a
+  // k pair (f32). Pair p of this thread: kap = p % 8 + 8 * (p / (8 * CPR)), nc = (p / 8) % CPR.
+  constexpr int KE = 128 / (int)sizeof(TI);          // k per K-tile
+  constexpr int CPR = BNB * (int)sizeof(TI) / 16;    // 16-byte chunks per row of the B tile
+  constexpr int NPAIR = KE / 2 * CPR / NT;           // pairs per thread
+  static_assert(!(KE / 2 * CPR % NT) && 2 * NPAIR <= B_PER, "B pair split");
+  const bool bkn = p.b_kn;
+  const __amdgpu_buffer_rsrc_t b_rsrc_kn =
+      make_rsrc(Bb + (int64_t)t.n0 * (int64_t)sizeof(TI),
+                (int)((int64_t)p.K * b_ld - (int64_t)t.n0 * (int64_t)sizeof(TI)));
 #pragma unroll
   for (int i = 0; i < A_PER; ++i) {
     const int c = tid + i * NT, r = c >> 3;
@@ -566,7 +577,21 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_reg_kernel(GemmA
   uint4 ra[A_PER], rb[B_PER];
   int ka = 0;  // byte offset of the next K-tile inside A's (possibly wrapped) row
   auto gload = [&](int kt) __attribute__((always_inline)) {
-    if (!seg2 || kt < KT1) {
+    if (bkn) {
+#pragma unroll
+      for (int i = 0; i < A_PER; ++i) ra[i] = buffer_load16(a_rsrc, a_voff[i], ka);
+#pragma unroll
+      for (int q = 0; q < NPAIR; ++q) {
+        const int pp = tid + q * NT;
+        const int kap = pp % 8 + 8 * (pp / (8 * CPR)), nc = (pp / 8) % CPR;
+        const int voff = 2 * kap * (int)b_ld + nc * 16;
+        const int soff = kt * KE * (int)b_ld;
+        rb[2 * q] = buffer_load16(b_rsrc_kn, voff, soff);
+        rb[2 * q + 1] = buffer_load16(b_rsrc_kn, voff + (int)b_ld, soff);
+      }
+      ka += 128;
+      if (ka == a_wrap) ka = 0;
+    } else if (!seg2 || kt < KT1) {
 #pragma unroll
       for (int i = 0; i < A_PER; ++i) ra[i] = buffer_load16(a_rsrc, a_voff[i], ka);
 #pragma unroll
@@ -584,6 +609,32 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_reg_kernel(GemmA
   };
   auto lstore = [&](int stage) __attribute__((always_inline)) {
     char* base = smem + stage * STAGE;
+    if (bkn) {
+#pragma unroll
+      for (int i = 0; i < A_PER; ++i) {
+        const int c = tid + i * NT;
+        *reinterpret_cast<uint4*>(base + (c >> 3) * kRowPitch + (c & 7) * 16) = ra[i];
+      }
+#pragma unroll
+      for (int q = 0; q < NPAIR; ++q) {
+        const int pp = tid + q * NT;
+        const int kap = pp % 8 + 8 * (pp / (8 * CPR)), nc = (pp / 8) % CPR;
+        const uint32_t* lo = reinterpret_cast<const uint32_t*>(&rb[2 * q]);
+        const uint32_t* hi = reinterpret_cast<const uint32_t*>(&rb[2 * q + 1]);
+        if constexpr (sizeof(TI) == 2) {  // 8 columns per chunk; word = (k even, k odd) of one column
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t a = (lo[j >> 1] >> (16 * (j & 1))) & 0xffffu, b = (hi[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+            *reinterpret_cast<uint32_t*>(base + A_BYTES + (nc * 8 + j) * kRowPitch + kap * 4) = a | (b << 16);
+          }
+        } else {  // 4 columns per chunk; (k even, k odd) of one column as 8 bytes
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<uint2*>(base + A_BYTES + (nc * 4 + j) * kRowPitch + kap * 8) = make_uint2(lo[j], hi[j]);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
       const int c = tid + i * NT;
@@ -848,6 +899,10 @@ hipError_t launch_gemm_split(const GemmArgs& a, int in_dtype, Epi epi, const Spl
 
 hipError_t launch_gemm(const GemmArgs& a, int in_dtype, Epi epi, GemmShape shape, hipStream_t s) {
   KernelTimer timer(a.tag ? a.tag : "gemm", s);
+  if (a.b_kn) {  // B stored [K, N]: register pipeline only, plain epilogues
+    if ((epi != Epi::Store && epi != Epi::AddF32) || a.A2 || a.koff || a.splits > 1) return hipErrorInvalidValue;
+    shape = GemmShape::Small;
+  }
   if (in_dtype == LMOE_BF16)
     return shape == GemmShape::Big ? launch_big<uint16_t>(a, epi, s) : launch_small<uint16_t>(a, epi, s);
   return shape == GemmShape::Big ? launch_big<float>(a, epi, s) : launch_small<float>(a, epi, s);

@@ -153,8 +153,6 @@ class LatentMoE:
         f32 = torch.float32
         if getattr(self, "_wt", None) is None:
             self._wt = {
-                "w1_t": torch.empty(E, L, 2 * I, dtype=dt, device=dev),
-                "w2_t": torch.empty(E, I, L, dtype=dt, device=dev),
                 "w_up_t": torch.empty(L, D, dtype=dt, device=dev),
                 "w_down_t": torch.empty(D, L, dtype=dt, device=dev),
                 "w2s_t": torch.empty(max(Ss, 1), D, dtype=dt, device=dev),
@@ -162,10 +160,9 @@ class LatentMoE:
             }
         wt = self._wt
         shared = S > 0
-        C.lmoe_bwd_transpose_weights(shape, w["w1"], w["w2"], w["w_up"], self.w2s_packed if shared else None,
-                                     self.w1s_packed if shared else None, w["w_down"], wt["w1_t"], wt["w2_t"],
-                                     wt["w_up_t"], wt["w2s_t"] if shared else None,
-                                     wt["w1s_t"] if shared else None, wt["w_down_t"])
+        C.lmoe_bwd_transpose_weights(shape, w["w_up"], self.w2s_packed if shared else None,
+                                     self.w1s_packed if shared else None, w["w_down"], wt["w_up_t"],
+                                     wt["w2s_t"] if shared else None, wt["w1s_t"] if shared else None, wt["w_down_t"])
         ws = {name: torch.empty(max(C.workspace_bytes(shape, which), 256), dtype=torch.uint8, device=dev)
               for name, which in (("up", C.LMOE_CALL_BWD_UP), ("comb", C.LMOE_CALL_BWD_COMBINE_NORM),
                                   ("exp", C.LMOE_CALL_BWD_EXPERTS), ("down", C.LMOE_CALL_BWD_DOWN),
@@ -197,8 +194,8 @@ class LatentMoE:
                                 w.get("gamma"), g["dy"], g["dl"], g["dl_sorted"], g["dgamma"], ws["comb"])
         C.lmoe_bwd_router(shape, x, w["w_router"], g["dl"], g["dl_sorted"], b["idx"], b["offsets"], b["sorted_token"],
                           g["dW_r"], g["dx"])
-        C.lmoe_bwd_experts(shape, b["x_lat"], b["sorted_token"], b["offsets"], w["w1"], wt["w1_t"], wt["w2_t"], b["h"],
-                           g["dy"], g["dh"], g["dgu"], g["dx_perm"], g["dW1"], g["dW2"], ws["exp"])
+        C.lmoe_bwd_experts(shape, b["x_lat"], b["sorted_token"], b["offsets"], w["w1"], w["w2"], b["h"], g["dy"],
+                           g["dh"], g["dgu"], g["dx_perm"], g["dW1"], g["dW2"], ws["exp"])
         C.lmoe_bwd_down(shape, x, g["dx_perm"], b["slot_of_pair"], wt["w_down_t"], g["dx_lat"], g["dW_dn"], g["dx"],
                         ws["down"])
         if shared:

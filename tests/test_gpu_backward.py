@@ -74,14 +74,14 @@ def test_backward_stages(name):
     W2s_p = np.concatenate(list(W2s), axis=1)
     xh = O.to_f64(inp["x"], dt)
 
-    wt = {"w1_t": torch.empty(E, L, 2 * I, dtype=tdt, device=dev), "w2_t": torch.empty(E, I, L, dtype=tdt, device=dev),
-          "w_up_t": torch.empty(L, D, dtype=tdt, device=dev), "w_down_t": torch.empty(D, L, dtype=tdt, device=dev),
+    wt = {"w_up_t": torch.empty(L, D, dtype=tdt, device=dev), "w_down_t": torch.empty(D, L, dtype=tdt, device=dev),
           "w2s_t": torch.empty(Ss, D, dtype=tdt, device=dev), "w1s_t": torch.empty(D, 2 * Ss, dtype=tdt, device=dev)}
-    C.lmoe_bwd_transpose_weights(shape, w["w1"], w["w2"], w["w_up"], layer.w2s_packed, layer.w1s_packed, w["w_down"],
-                                 wt["w1_t"], wt["w2_t"], wt["w_up_t"], wt["w2s_t"], wt["w1s_t"], wt["w_down_t"])
+    C.lmoe_bwd_transpose_weights(shape, w["w_up"], layer.w2s_packed, layer.w1s_packed, w["w_down"], wt["w_up_t"],
+                                 wt["w2s_t"], wt["w1s_t"], wt["w_down_t"])
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(host(wt["w1_t"]), host(w["w1"]).transpose(0, 2, 1))
+    np.testing.assert_array_equal(host(wt["w_up_t"]), host(w["w_up"]).T)
     np.testing.assert_array_equal(host(wt["w2s_t"]), host(layer.w2s_packed).T)
+    np.testing.assert_array_equal(host(wt["w1s_t"]), host(layer.w1s_packed).T)
     ws = lambda which: torch.empty(max(C.workspace_bytes(shape, which), 256), dtype=torch.uint8, device=dev)  # noqa
 
     # B1: up-projection
@@ -143,8 +143,8 @@ def test_backward_stages(name):
     dx_perm = torch.empty(rows, L, dtype=tdt, device=dev)
     dW1 = torch.empty(E, 2 * I, L, dtype=f32, device=dev)
     dW2 = torch.empty(E, L, I, dtype=f32, device=dev)
-    C.lmoe_bwd_experts(shape, b["x_lat"], b["sorted_token"], b["offsets"], w["w1"], wt["w1_t"], wt["w2_t"], b["h"], dy,
-                       dh, dgu, dx_perm, dW1, dW2, ws(C.LMOE_CALL_BWD_EXPERTS))
+    C.lmoe_bwd_experts(shape, b["x_lat"], b["sorted_token"], b["offsets"], w["w1"], w["w2"], b["h"], dy, dh, dgu,
+                       dx_perm, dW1, dW2, ws(C.LMOE_CALL_BWD_EXPERTS))
     torch.cuda.synchronize()
     off = host(b["offsets"]).astype(np.int64)
     st = host(b["sorted_token"]).astype(np.int64)
