@@ -40,7 +40,7 @@ size_t ws_combine(const lmoe_shape* sh) {  // block partials of dgamma and their
   return round_up((blocks + (blocks + 63) / 64) * sh->d_latent * sizeof(float));
 }
 size_t ws_experts(const lmoe_shape* sh) {
-  const size_t idx = 3 * round_up((size_t)(sh->n_experts + 1) * 4);
+  const size_t idx = 2 * round_up((size_t)(sh->n_experts + 1) * 4);
   const size_t rows = (size_t)(sh->d_latent + sh->inter + 2 * sh->inter + sh->d_latent);
   return idx + round_up(rows * kpad(sh) * esize(sh->act_dtype));
 }
@@ -217,10 +217,9 @@ lmoe_status lmoe_bwd_experts(const lmoe_shape* sh, const void* x_lat, const int3
   const int64_t Kp = kpad(sh);
   char* ws = static_cast<char*>(workspace);
   const size_t ia = round_up((size_t)(E + 1) * 4);
-  int32_t* mts = reinterpret_cast<int32_t*>(ws);                // m-tile prefix of the recomputed GEMM1
-  int32_t* mts128 = reinterpret_cast<int32_t*>(ws + ia);        // 128-row m-tile prefix ([K, N] weights)
-  int32_t* ptile = reinterpret_cast<int32_t*>(ws + 2 * ia);     // 64-row tile prefix (padded K ranges)
-  char* tb = ws + 3 * ia;
+  int32_t* mts = reinterpret_cast<int32_t*>(ws);                // m-tile prefix of the grouped GEMMs
+  int32_t* ptile = reinterpret_cast<int32_t*>(ws + ia);         // 64-row tile prefix (padded K ranges)
+  char* tb = ws + 2 * ia;
   void* dy_t = tb;                                       // [L, Kp]
   void* h_t = tb + (size_t)L * Kp * esz;                 // [I, Kp]
   void* dgu_t = tb + (size_t)(L + I) * Kp * esz;         // [2I, Kp]
@@ -228,7 +227,6 @@ lmoe_status lmoe_bwd_experts(const lmoe_shape* sh, const void* x_lat, const int3
   // with no rows every K-range is empty and the K-grouped GEMMs write zero gradients
   const GemmShape gshape = (int64_t)rows >= (int64_t)E * 64 ? GemmShape::Big : GemmShape::Small;
   st = hip_status(launch_mtile_prefix(expert_offsets, E, gemm_block_m(gshape), mts, s));
-  if (st == LMOE_OK) st = hip_status(launch_mtile_prefix(expert_offsets, E, 128, mts128, s));
   if (st == LMOE_OK) st = hip_status(launch_mtile_prefix(expert_offsets, E, 64, ptile, s));
   if (st != LMOE_OK) return st;
   auto grouped = [&](const void* A, int64_t lda, const void* B, int64_t ldb, int64_t bstride, void* C, int64_t ldc,
@@ -275,9 +273,8 @@ lmoe_status lmoe_bwd_experts(const lmoe_shape* sh, const void* x_lat, const int3
   // dh = dy . W2_e, W2_e read as [K = L, N = I]
   if (rows > 0) {
     GemmArgs a = grouped(dy_perm, L, w2, I, (int64_t)L * I, dh, I, I, L, "bwd_gemm_dh");
-    a.mtile_start = mts128;
     a.b_kn = true;
-    st = hip_status(launch_gemm(a, dt, Epi::Store, GemmShape::Small, s));
+    st = hip_status(launch_gemm(a, dt, Epi::Store, dt == LMOE_BF16 ? gshape : GemmShape::Small, s));
   }
   // dW2_e = dy_e^T h_e
   if (st == LMOE_OK)
@@ -300,9 +297,8 @@ lmoe_status lmoe_bwd_experts(const lmoe_shape* sh, const void* x_lat, const int3
   // dx_perm = d[g | u] . W1_e, W1_e read as [K = 2I, N = L]
   if (st == LMOE_OK && rows > 0) {
     GemmArgs a = grouped(dgu, 2 * I, w1, L, (int64_t)2 * I * L, dx_perm, L, L, 2 * I, "bwd_gemm_dx_experts");
-    a.mtile_start = mts128;
     a.b_kn = true;
-    st = hip_status(launch_gemm(a, dt, Epi::Store, GemmShape::Small, s));
+    st = hip_status(launch_gemm(a, dt, Epi::Store, dt == LMOE_BF16 ? gshape : GemmShape::Small, s));
   }
   // dW1_e = d[g | u]_e^T x_perm_e (x_perm gathered from x_lat through sorted_token)
   if (st == LMOE_OK)

@@ -308,7 +308,10 @@ __device__ inline void dispatch_na(int na, F&& f) {
 // ------------------------------------------------------------------------------------------------
 // DMA pipeline: 256x256 tiles, LDS fed straight from HBM, three K-tiles in flight
 // ------------------------------------------------------------------------------------------------
-template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, int NS, int KB, Epi EPI>
+// BKN: B is stored [K, N] (bf16): a K-tile of B is 64 rows of BNB columns, DMA'd row by row into
+// LDS with the 16-byte chunk c of row k at slot c ^ (k % 16); a B fragment (8 consecutive k of one
+// column) is gathered with 16-bit LDS reads, which the swizzle spreads over distinct banks.
+template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, int NS, int KB, Epi EPI, bool BKN = false>
 __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_dma_kernel(GemmArgs p) {
   constexpr int NW = WAVES_M * WAVES_N;
@@ -346,7 +349,11 @@ gemm_dma_kernel(GemmArgs p) {
   const u32x4 a_desc = gather ? make_desc(p.A, (int)(p.a_nrows * a_ld))
                               : make_desc(static_cast<const char*>(p.A) + (int64_t)t.row0 * a_ld +
                                               (int64_t)t.k0 * (int64_t)sizeof(TI), (int)(t.rows * a_ld));
-  const u32x4 b_desc0 = make_desc(Bb + (int64_t)t.n0 * b_ld, (int)(ncols * b_ld));
+  static_assert(!BKN || (sizeof(TI) == 2 && KB == 128 && !GLU && EPI == Epi::Store), "[K, N] B: bf16 store");
+  constexpr int BROW = BNB * (int)sizeof(TI);  // bytes of one k-row of a [K, N] B tile
+  const u32x4 b_desc0 = BKN ? make_desc(Bb + (int64_t)t.n0 * (int64_t)sizeof(TI),
+                                        (int)((int64_t)p.K * b_ld - (int64_t)t.n0 * (int64_t)sizeof(TI)))
+                            : make_desc(Bb + (int64_t)t.n0 * b_ld, (int)(ncols * b_ld));
   const u32x4 b_desc1 = GLU ? make_desc(Bb + (int64_t)(p.glu_up_off + t.n0) * b_ld, (int)(ncols * b_ld)) : b_desc0;
   const u32x4 a2_desc =
       seg2 ? make_desc(static_cast<const char*>(p.A2) + (int64_t)t.row0 * a_ld2, (int)(t.rows * a_ld2)) : a_desc;
@@ -374,10 +381,16 @@ gemm_dma_kernel(GemmArgs p) {
   }
 #pragma unroll
   for (int i = 0; i < B_PW; ++i) {
-    const int r = (wave * B_PW + i) * RPD + lr;
-    const int ch = (slot ^ swz<KB>(r)) * 16;
-    b_voff[i] = (r % BNO) * (int)b_ld + ch;
-    b2_voff[i] = (r % BNO) * (int)b_ld2 + ch;
+    if constexpr (BKN) {  // block j holds k-rows 2j and 2j + 1; lane l fills slot l % 32 of row 2j + l / 32
+      const int k = 2 * (wave * B_PW + i) + lane / 32;
+      b_voff[i] = k * (int)b_ld + (((lane % 32) ^ (k % 16)) * 16);
+      b2_voff[i] = b_voff[i];
+    } else {
+      const int r = (wave * B_PW + i) * RPD + lr;
+      const int ch = (slot ^ swz<KB>(r)) * 16;
+      b_voff[i] = (r % BNO) * (int)b_ld + ch;
+      b2_voff[i] = (r % BNO) * (int)b_ld2 + ch;
+    }
   }
   const unsigned lds0 = __builtin_amdgcn_readfirstlane(
       (unsigned)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
@@ -391,7 +404,8 @@ gemm_dma_kernel(GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < B_PW; ++i) {
         const bool up = GLU && (wave * B_PW + i) * RPD >= BNO;
-        dma16(up ? b_desc1 : b_desc0, b_voff[i], kt * KB, base + A_BYTES + (wave * B_PW + i) * 1024);
+        dma16(up ? b_desc1 : b_desc0, b_voff[i], BKN ? kt * (KB / (int)sizeof(TI)) * (int)b_ld : kt * KB,
+              base + A_BYTES + (wave * B_PW + i) * 1024);
       }
       ka += KB;
       if (ka == a_wrap) ka = 0;
@@ -434,7 +448,18 @@ gemm_dma_kernel(GemmArgs p) {
         for (int j = 0; j < WN; ++j) {
           const int ocb = (j % WNO) * WAVES_N + wn;
           const int bblk = (GLU && j >= WNO) ? BNO / 32 + ocb : ocb;
-          b[j] = *reinterpret_cast<const uint4*>(base + A_BYTES + bblk * 32 * KB + fo[s]);
+          if constexpr (BKN) {
+            const int n = bblk * 32 + (lane & 31), c = n >> 3, e = n & 7;
+            const int k0 = s * 16 + 8 * (lane >> 5);
+            uint16_t v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              v[i] = *reinterpret_cast<const uint16_t*>(base + A_BYTES + (k0 + i) * BROW + ((c ^ ((k0 + i) & 15)) << 4) +
+                                                        e * 2);
+            b[j] = *reinterpret_cast<const uint4*>(v);
+          } else {
+            b[j] = *reinterpret_cast<const uint4*>(base + A_BYTES + bblk * 32 * KB + fo[s]);
+          }
         }
       };
       load(0, af[0], bf[0]);
@@ -773,6 +798,12 @@ hipError_t launch_big(const GemmArgs& a, Epi epi, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(8 * kWave);
+  if (a.b_kn) {
+    if constexpr (sizeof(TI) == 2)
+      hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Store, true>), grid, block, 0, s,
+                         a);
+    return hipGetLastError();
+  }
   LMOE_LAUNCH_EPI(gemm_dma_kernel, TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes)
   return hipGetLastError();
 }
@@ -899,9 +930,9 @@ hipError_t launch_gemm_split(const GemmArgs& a, int in_dtype, Epi epi, const Spl
 
 hipError_t launch_gemm(const GemmArgs& a, int in_dtype, Epi epi, GemmShape shape, hipStream_t s) {
   KernelTimer timer(a.tag ? a.tag : "gemm", s);
-  if (a.b_kn) {  // B stored [K, N]: register pipeline only, plain epilogues
+  if (a.b_kn) {  // B stored [K, N]: plain epilogues; the DMA pipeline takes bf16 stores only
     if ((epi != Epi::Store && epi != Epi::AddF32) || a.A2 || a.koff || a.splits > 1) return hipErrorInvalidValue;
-    shape = GemmShape::Small;
+    if (in_dtype != LMOE_BF16 || epi != Epi::Store) shape = GemmShape::Small;
   }
   if (in_dtype == LMOE_BF16)
     return shape == GemmShape::Big ? launch_big<uint16_t>(a, epi, s) : launch_small<uint16_t>(a, epi, s);

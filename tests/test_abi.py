@@ -123,9 +123,9 @@ def test_backward_workspace_and_validation(lib):
     for which in (C.LMOE_CALL_BWD_UP, C.LMOE_CALL_BWD_COMBINE_NORM, C.LMOE_CALL_BWD_EXPERTS, C.LMOE_CALL_BWD_DOWN,
                   C.LMOE_CALL_BWD_SHARED):
         assert C.workspace_bytes(k3, which) > 0
-    # experts: three tile prefixes, then [L + I + 2I + L] x (T*k + 64 E) transposed activations
+    # experts: two tile prefixes, then [L + I + 2I + L] x (T*k + 64 E) transposed activations
     kp = 8192 * 16 + 64 * 896
-    assert C.workspace_bytes(k3, C.LMOE_CALL_BWD_EXPERTS) == 3 * 3840 + (3584 * 2 + 3 * 512) * kp * 2
+    assert C.workspace_bytes(k3, C.LMOE_CALL_BWD_EXPERTS) == 2 * 3840 + (3584 * 2 + 3 * 512) * kp * 2
     big = C.make_shape(CONFIGS["k3_prefill"])
     big.d_latent = 4096 + 64                                   # past the combine backward row limit (bf16)
     null = None
