@@ -57,19 +57,32 @@ __global__ void __launch_bounds__(256) combine_norm_kernel(const T* __restrict__
   for (int i = 0; i < CPL; ++i)
 #pragma unroll
     for (int v = 0; v < V; ++v) z[i][v] = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const int32_t slot = slot_of_pair[t * k + j];
-    if (slot < 0) continue;
-    const float wj = w[t * k + j];
-    const T* row = y + (int64_t)slot * L;
+  // two rows in flight per step; the sum still runs in rank order j = 0, 1, 2, ...
+  for (int j = 0; j < k; j += 2) {
+    const bool two = j + 1 < k;
+    const int32_t s0 = slot_of_pair[t * k + j], s1 = two ? slot_of_pair[t * k + j + 1] : -1;
+    const float w0 = w[t * k + j], w1 = two ? w[t * k + j + 1] : 0.0f;
+    uint4 r0[CPL], r1[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = lane + 64 * i;
-      if (c < chunks) {
-        float f[V];
-        Vec<T>::unpack(*reinterpret_cast<const uint4*>(row + (int64_t)c * V), f);
+      r0[i] = (c < chunks && s0 >= 0) ? *reinterpret_cast<const uint4*>(y + (int64_t)s0 * L + (int64_t)c * V)
+                                      : make_uint4(0, 0, 0, 0);
+      r1[i] = (c < chunks && s1 >= 0) ? *reinterpret_cast<const uint4*>(y + (int64_t)s1 * L + (int64_t)c * V)
+                                      : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-        for (int v = 0; v < V; ++v) z[i][v] += wj * f[v];
+    for (int i = 0; i < CPL; ++i) {
+      float f[V];
+      if (s0 >= 0) {
+        Vec<T>::unpack(r0[i], f);
+#pragma unroll
+        for (int v = 0; v < V; ++v) z[i][v] += w0 * f[v];
+      }
+      if (s1 >= 0) {
+        Vec<T>::unpack(r1[i], f);
+#pragma unroll
+        for (int v = 0; v < V; ++v) z[i][v] += w1 * f[v];
       }
     }
   }
