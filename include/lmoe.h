@@ -59,7 +59,7 @@ enum {
   LMOE_CALL_ROUTE = 0, LMOE_CALL_PERMUTE = 1, LMOE_CALL_GROUPED_GLU = 2, LMOE_CALL_COMBINE_NORM_UP = 3,
   /* backward calls */
   LMOE_CALL_BWD_UP = 16, LMOE_CALL_BWD_COMBINE_NORM = 17, LMOE_CALL_BWD_EXPERTS = 18, LMOE_CALL_BWD_DOWN = 19,
-  LMOE_CALL_BWD_SHARED = 20
+  LMOE_CALL_BWD_SHARED = 20, LMOE_CALL_GROUPED_GLU_MX = 32
 };
 
 /* Bytes of workspace `which_call` needs for this shape (0 when none). For LMOE_CALL_GROUPED_GLU
@@ -256,6 +256,45 @@ lmoe_status lmoe_bwd_down(const lmoe_shape* shape, const void* x, const void* dx
 lmoe_status lmoe_bwd_shared(const lmoe_shape* shape, const void* x, const void* w1s_packed, const void* w1s_t,
                             const void* dh_shared, void* dgu_shared, float* dw1s_packed, float* dx, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* ================================================================================================
+ * MX formats for the routed experts ([slm] 训练基础设施: MXFP4 weights with MXFP8 activations).
+ * The pages name the formats only; these calls follow the OCP Microscaling definitions: blocks of
+ * 32 consecutive elements along the contraction dimension share an E8M0 scale byte e (value
+ * 2^(e - 127)); the shared exponent is floor(log2(block max)) - emax (emax 2 for FP4 E2M1, 8 for
+ * FP8 E4M3), clamped to [-127, 127], 0 for an all-zero block; each element is v / 2^(e - 127)
+ * rounded to nearest, ties to the even significand, saturated at the largest normal (6, 448).
+ * ============================================================================================== */
+enum { LMOE_MX_FP4 = 4, LMOE_MX_FP8 = 8 };
+
+/* MX quantisation of the rows of x [rows, K] (act_dtype, K a multiple of 32) along K.
+ *   fmt LMOE_MX_FP4: codes [rows, K/2] u8, two E2M1 codes per byte, element 2i in the low nibble
+ *   fmt LMOE_MX_FP8: codes [rows, K] u8, one E4M3 code per byte (NaN codes never produced)
+ *   scales [rows, K/32] u8 E8M0 bytes. x and codes 16-byte aligned.
+ * Routed weights: w1 as rows = E*2I, K = L; w2 as rows = E*L, K = I (one-time, per weight change). */
+lmoe_status lmoe_mx_quantize(const lmoe_shape* shape, int32_t fmt, int64_t rows, int32_t K, const void* x,
+                             void* codes, void* scales, void* stream);
+
+/* A7 + A8 with MX operands: the routed experts of lmoe_grouped_situ_glu on MXFP8 activations and
+ * MXFP4 weights (bf16 act_dtype only). Per group g:
+ *   [g | u] = deq(A[rows]) . deq(w1[g])^T ;  h = SiTU-GLU (f32, stored bf16) ;
+ *   h is MX-quantised to FP8 along inter ;  y[rows] = deq(hq[rows]) . deq(w2[g])^T (stored bf16)
+ * The products run on the scaled MFMA with f32 accumulation.
+ *   K, inter      multiples of 128
+ *   a_codes       [a_rows, K] FP8 codes, a_scales [a_rows, K/32] (lmoe_mx_quantize of x_lat, fmt FP8)
+ *   a_row_index, group_offsets, a_rows, rows, n_groups, n_out: as lmoe_grouped_situ_glu
+ *   w1_codes      [G, 2*inter, K/2] FP4 (packed), w1_scales [G, 2*inter, K/32]
+ *   w2_codes      [G, n_out, inter/2] FP4 (packed), w2_scales [G, n_out, inter/32]
+ *   h             [rows, inter] bf16 (out), y [rows, n_out] bf16 (out)
+ *   workspace     at least lmoe_workspace_bytes(shape, LMOE_CALL_GROUPED_GLU_MX) for rows = T*k,
+ *                 inter = shape inter: the tile list and the FP8 copy of h with its scales
+ * a_codes must be under 2 GiB (31-bit byte offsets). Codes 16-byte and scales 4-byte aligned.   */
+lmoe_status lmoe_grouped_situ_glu_mx(const lmoe_shape* shape, int32_t n_groups, int32_t rows, int32_t K,
+                                     int32_t inter, int32_t n_out, const void* a_codes, const void* a_scales,
+                                     int32_t a_rows, const int32_t* a_row_index, const int32_t* group_offsets,
+                                     const void* w1_codes, const void* w1_scales, const void* w2_codes,
+                                     const void* w2_scales, void* h, void* y, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* Kernel timing for measurement. When enabled, every kernel the library enqueues is bracketed by
  * HIP events on its stream. lmoe_profile_collect() synchronises those events and folds them into

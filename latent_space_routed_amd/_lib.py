@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "liblmoe.so")
 LMOE_OK, LMOE_ERR_INVALID_ARGUMENT, LMOE_ERR_UNSUPPORTED, LMOE_ERR_WORKSPACE, LMOE_ERR_HIP = range(5)
 LMOE_F32, LMOE_BF16 = 0, 1
 LMOE_CALL_ROUTE, LMOE_CALL_PERMUTE, LMOE_CALL_GROUPED_GLU, LMOE_CALL_COMBINE_NORM_UP = 0, 1, 2, 3
+LMOE_CALL_GROUPED_GLU_MX = 32
 LMOE_CALL_BWD_UP, LMOE_CALL_BWD_COMBINE_NORM, LMOE_CALL_BWD_EXPERTS, LMOE_CALL_BWD_DOWN, LMOE_CALL_BWD_SHARED = \
     16, 17, 18, 19, 20
 
@@ -24,7 +25,7 @@ LMOE_CALL_BWD_UP, LMOE_CALL_BWD_COMBINE_NORM, LMOE_CALL_BWD_EXPERTS, LMOE_CALL_B
 EXPORTS = ("lmoe_workspace_bytes", "lmoe_status_string", "lmoe_route", "lmoe_qb_histogram", "lmoe_qb_update",
            "lmoe_permute", "lmoe_grouped_situ_glu", "lmoe_pack_shared", "lmoe_combine_norm_up",
            "lmoe_bwd_transpose_weights", "lmoe_bwd_up", "lmoe_bwd_combine_norm", "lmoe_bwd_router",
-           "lmoe_bwd_experts", "lmoe_bwd_down", "lmoe_bwd_shared",
+           "lmoe_bwd_experts", "lmoe_bwd_down", "lmoe_bwd_shared", "lmoe_mx_quantize", "lmoe_grouped_situ_glu_mx",
            "lmoe_profile_enable", "lmoe_profile_reset", "lmoe_profile_collect", "lmoe_profile_get")
 
 
@@ -80,6 +81,10 @@ def lib() -> ctypes.CDLL:
             "lmoe_bwd_experts": (ctypes.c_int, [_S] + [_P] * 13 + [ctypes.c_size_t, _P]),
             "lmoe_bwd_down": (ctypes.c_int, [_S] + [_P] * 8 + [ctypes.c_size_t, _P]),
             "lmoe_bwd_shared": (ctypes.c_int, [_S] + [_P] * 8 + [ctypes.c_size_t, _P]),
+            "lmoe_mx_quantize": (ctypes.c_int, [_S, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, _P, _P, _P, _P]),
+            "lmoe_grouped_situ_glu_mx": (ctypes.c_int, [_S, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                         ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32, _P,
+                                                         _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "lmoe_profile_enable": (None, [ctypes.c_int]),
             "lmoe_profile_reset": (None, []),
             "lmoe_profile_collect": (ctypes.c_int, []),
@@ -222,6 +227,22 @@ def lmoe_bwd_down(shape, x, dx_perm, slot_of_pair, w_down_t, dx_lat, dw_down, dx
 
 def lmoe_bwd_shared(shape, x, w1s_packed, w1s_t, dh_shared, dgu_shared, dw1s_packed, dx, workspace):
     _call("lmoe_bwd_shared", shape, x, w1s_packed, w1s_t, dh_shared, dgu_shared, dw1s_packed, dx, (workspace, "ws"))
+
+
+LMOE_MX_FP4, LMOE_MX_FP8 = 4, 8
+
+
+def lmoe_mx_quantize(shape, fmt: int, rows: int, K: int, x, codes, scales, stream=None):
+    _check("lmoe_mx_quantize", lib().lmoe_mx_quantize(ctypes.byref(shape), int(fmt), int(rows), int(K), _ptr(x),
+                                                      _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def lmoe_grouped_situ_glu_mx(shape, G, rows, K, inter, n_out, a_codes, a_scales, a_rows, a_row_index, group_offsets,
+                             w1_codes, w1_scales, w2_codes, w2_scales, h, y, workspace, stream=None):
+    _check("lmoe_grouped_situ_glu_mx", lib().lmoe_grouped_situ_glu_mx(
+        ctypes.byref(shape), int(G), int(rows), int(K), int(inter), int(n_out), _ptr(a_codes), _ptr(a_scales),
+        int(a_rows), _ptr(a_row_index), _ptr(group_offsets), _ptr(w1_codes), _ptr(w1_scales), _ptr(w2_codes),
+        _ptr(w2_scales), _ptr(h), _ptr(y), _ptr(workspace), _nbytes(workspace), _stream(stream)))
 
 
 def profile_enable(on: bool) -> None:

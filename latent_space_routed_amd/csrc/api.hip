@@ -57,6 +57,10 @@ size_t permute_ws(const lmoe_shape* sh) {
   return round_up((size_t)ceil_div(sh->T > 0 ? sh->T : 1, kPermChunk) * sh->n_experts * 4);
 }
 size_t glu_ws(int groups) { return round_up((size_t)(groups + 1) * 4); }
+// tile list, then the FP8 codes and the scales of h
+size_t mx_glu_ws(int groups, int64_t rows, int inter) {
+  return glu_ws(groups) + round_up((size_t)rows * inter) + round_up((size_t)rows * (inter / 32));
+}
 
 // Split-K plans of the dense GEMMs behind each call (no split once the batch fills the chip).
 SplitPlan router_plan(const lmoe_shape* sh) {
@@ -123,6 +127,8 @@ size_t lmoe_workspace_bytes(const lmoe_shape* sh, int which) {
     case LMOE_CALL_PERMUTE: return permute_ws(sh) + split_bytes(down_plan(sh), sh->T, sh->d_latent);
     case LMOE_CALL_GROUPED_GLU: return glu_ws(sh->n_experts > 1 ? sh->n_experts : 1) + shared_split_bytes(sh);
     case LMOE_CALL_COMBINE_NORM_UP: return combine_split_bytes(sh);
+    case LMOE_CALL_GROUPED_GLU_MX:
+      return mx_glu_ws(sh->n_experts > 1 ? sh->n_experts : 1, (int64_t)sh->T * sh->top_k, sh->inter);
     default: return bwd_workspace_bytes(sh, which);
   }
 }
@@ -377,6 +383,96 @@ lmoe_status lmoe_combine_norm_up(const lmoe_shape* sh, const void* y_perm, const
   float* part = split_region(sp, T, D, workspace, workspace_bytes, 0);
   return hip_status(run_gemm(a, sh->act_dtype, y_shared ? Epi::AddF32 : Epi::Store, dense_shape(T, ceil_div(D, 256)),
                              sp, part, s));
+}
+
+lmoe_status lmoe_mx_quantize(const lmoe_shape* sh, int32_t fmt, int64_t rows, int32_t K, const void* x, void* codes,
+                             void* scales, void* stream) {
+  lmoe_status st = check_shape(sh);
+  if (st != LMOE_OK) return st;
+  if ((fmt != LMOE_MX_FP4 && fmt != LMOE_MX_FP8) || rows < 0 || K <= 0) return LMOE_ERR_INVALID_ARGUMENT;
+  if (K % 32) return LMOE_ERR_UNSUPPORTED;
+  if (rows == 0) return LMOE_OK;
+  if (!aligned16(x) || !aligned16(codes) || !scales) return LMOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_mx_quantize(x, sh->act_dtype, rows * (int64_t)(K / 32), fmt == LMOE_MX_FP4, codes, scales,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+lmoe_status lmoe_grouped_situ_glu_mx(const lmoe_shape* sh, int32_t G, int32_t rows, int32_t K, int32_t inter,
+                                     int32_t n_out, const void* a_codes, const void* a_scales, int32_t a_rows,
+                                     const int32_t* a_row_index, const int32_t* group_offsets, const void* w1_codes,
+                                     const void* w1_scales, const void* w2_codes, const void* w2_scales, void* h,
+                                     void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  lmoe_status st = check_shape(sh);
+  if (st != LMOE_OK) return st;
+  if (sh->act_dtype != LMOE_BF16) return LMOE_ERR_UNSUPPORTED;
+  if (G < 1 || rows < 0 || a_rows < 0 || K <= 0 || inter <= 0 || n_out <= 0) return LMOE_ERR_INVALID_ARGUMENT;
+  if (K % 128 || inter % 128 || n_out % 8) return LMOE_ERR_UNSUPPORTED;
+  if (!group_offsets && G != 1) return LMOE_ERR_INVALID_ARGUMENT;
+  if (!a_row_index && a_rows != rows) return LMOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)a_rows * K > 0x7fff0000LL || (int64_t)rows * inter > 0x7fff0000LL) return LMOE_ERR_UNSUPPORTED;
+  if (rows == 0) return LMOE_OK;
+  if (!aligned16(a_codes) || !aligned4(a_scales) || !aligned16(w1_codes) || !aligned4(w1_scales) ||
+      !aligned16(w2_codes) || !aligned4(w2_scales) || !aligned16(h) || !aligned16(y) ||
+      (a_row_index && !aligned4(a_row_index)) || (group_offsets && !aligned4(group_offsets)))
+    return LMOE_ERR_INVALID_ARGUMENT;
+  const size_t need = mx_glu_ws(G, rows, inter);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return LMOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* mts = reinterpret_cast<int32_t*>(ws);
+  uint8_t* h_codes = reinterpret_cast<uint8_t*>(ws + glu_ws(G));
+  uint8_t* h_scales = h_codes + round_up((size_t)rows * inter);
+  if (group_offsets) {
+    st = hip_status(launch_mtile_prefix(group_offsets, G, gemm_block_m(GemmShape::Big), mts, s));
+    if (st != LMOE_OK) return st;
+  }
+  GemmArgs g1 = gemm_args();
+  g1.A = a_codes;
+  g1.lda = K;  // bytes of FP8 codes
+  g1.a_kwrap = K;
+  g1.a_scale = static_cast<const uint8_t*>(a_scales);
+  g1.a_rows = a_row_index;
+  g1.a_nrows = a_rows;
+  g1.B = w1_codes;
+  g1.ldb = K / 2;  // bytes of packed FP4 codes
+  g1.b_gstride = (int64_t)2 * inter * (K / 2);
+  g1.b_scale = static_cast<const uint8_t*>(w1_scales);
+  g1.b_scale_gstride = (int64_t)2 * inter * (K / 32);
+  g1.C = h;
+  g1.ldc = inter;
+  g1.c_dtype = LMOE_BF16;
+  g1.goff = group_offsets;
+  g1.mtile_start = group_offsets ? mts : nullptr;
+  g1.G = G;
+  g1.M = rows;
+  g1.N = inter;
+  g1.K = K;
+  g1.glu_up_off = inter;
+  g1.beta1 = sh->beta1;
+  g1.beta2 = sh->beta2;
+  g1.tag = "gemm_glu_mx";
+  st = hip_status(launch_gemm_mx(g1, Epi::Glu, s));
+  if (st != LMOE_OK) return st;
+  st = hip_status(launch_mx_quantize(h, LMOE_BF16, (int64_t)rows * (inter / 32), false, h_codes, h_scales, s));
+  if (st != LMOE_OK) return st;
+  GemmArgs g2 = g1;
+  g2.A = h_codes;
+  g2.lda = inter;
+  g2.a_kwrap = inter;
+  g2.a_scale = h_scales;
+  g2.a_rows = nullptr;
+  g2.a_nrows = rows;
+  g2.B = w2_codes;
+  g2.ldb = inter / 2;
+  g2.b_gstride = (int64_t)n_out * (inter / 2);
+  g2.b_scale = static_cast<const uint8_t*>(w2_scales);
+  g2.b_scale_gstride = (int64_t)n_out * (inter / 32);
+  g2.C = y;
+  g2.ldc = n_out;
+  g2.N = n_out;
+  g2.K = inter;
+  g2.tag = "gemm_down_mx";
+  return hip_status(launch_gemm_mx(g2, Epi::Store, s));
 }
 
 }  // extern "C"

@@ -144,6 +144,11 @@ struct GemmArgs {
   // register pipeline transposes it on its way into LDS. Store / AddF32 epilogues, no second K
   // segment, no split.
   bool b_kn;
+  // MX operands (launch_gemm_mx): E8M0 scale bytes [rows, K/32] of A and [N, K/32] of each B group
+  // (b_scale_gstride bytes apart); A, B, lda, ldb and b_gstride then count bytes of element codes.
+  const uint8_t* a_scale;
+  const uint8_t* b_scale;
+  int64_t b_scale_gstride;
 };
 
 // K-split of a dense GEMM on few rows (decode-size batches), so that its register-pipeline tiles
@@ -168,6 +173,13 @@ hipError_t launch_mtile_prefix(const int32_t* goff, int G, int bm, int32_t* mtil
 // shape validation shared by the forward and backward calls (api.hip); backward workspace sizes
 lmoe_status validate_shape(const lmoe_shape* sh);
 size_t bwd_workspace_bytes(const lmoe_shape* sh, int which);
+
+hipError_t launch_gemm_mx(const GemmArgs& a, Epi epi, hipStream_t s);
+
+// MX quantisation (mx.hip): nblocks blocks of 32 elements of x (act dtype) -> FP4 (packed) or FP8
+// codes and E8M0 scale bytes
+hipError_t launch_mx_quantize(const void* x, int dtype, int64_t nblocks, bool fp4, void* codes, void* scales,
+                              hipStream_t s);
 
 // backward (backward.hip)
 hipError_t launch_transpose(const void* in, void* out, int batch, int R, int C, int64_t in_bstride,

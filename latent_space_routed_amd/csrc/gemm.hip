@@ -501,6 +501,217 @@ gemm_dma_kernel(GemmArgs p) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// MX pipeline: FP8 (E4M3) A x FP4 (E2M1) B with E8M0 scales per 32 k, on
+// v_mfma_scale_f32_32x32x64_f8f6f4 (the block scales are applied inside the MFMA)
+// ------------------------------------------------------------------------------------------------
+// Same 256x256 tiles, DMA ring and XCD-contiguous numbering as the bf16 DMA pipeline, with a K-tile
+// of 128 k: 128 bytes of every A row, 64 bytes of every B row and one dword of four scale bytes per
+// row of each, so a K-tile is 7 DMA instructions per wave. Operand layout of the 32x32x64 step
+// (lane l: row or column l % 32, half h = l / 32):
+//   A fp8: bytes 0..15 hold k in [16h, 16h + 16), bytes 16..31 k in [32 + 16h, 48 + 16h) -- two
+//          16-byte LDS reads, chunks h and h + 2 of the step's 64 bytes;
+//   B fp4: 16 bytes, 32 nibbles (low nibble first) of k in [32h, 32h + 32) -- chunk h of the
+//          step's 32 bytes;
+//   scales: lane (r, h) supplies the scale of 32-k block h of the step for row (column) r.
+// A and B rows carry the same swizzle as the bf16 pipeline (key r/2 % 8 for 128-byte rows, r/4 % 4
+// for 64-byte rows), which keeps both fragment reads free of bank conflicts.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ inline void dma4(const u32x4& desc, int voff, int soff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(desc), "s"(soff)
+               : "memory", "m0");
+}
+
+constexpr int kMxK = 128;  // k per K-tile of the MX pipeline
+
+template <int WAVES_M, int WAVES_N, int WM, int WN, int NS, Epi EPI>
+__global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+gemm_mx_kernel(GemmArgs p) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int BM = WAVES_M * WM * 32;
+  constexpr int BNB = WAVES_N * WN * 32;
+  constexpr bool GLU = EPI == Epi::Glu;
+  static_assert(EPI == Epi::Store || GLU, "MX pipeline: plain or GLU stores");
+  static_assert(!GLU || WN % 2 == 0, "GLU needs gate/up column-block pairs");
+  constexpr int BNO = GLU ? BNB / 2 : BNB;
+  constexpr int KA = kMxK, KBB = kMxK / 2;   // bytes per row per K-tile: A (fp8), B (fp4)
+  constexpr int RPA = 1024 / KA, RPB = 1024 / KBB;
+  constexpr int A_PW = BM / RPA / NW, B_PW = BNB / RPB / NW;
+  static_assert(A_PW * RPA * NW == BM && B_PW * RPB * NW == BNB, "DMA split");
+  static_assert(!GLU || BNO % RPB == 0, "a DMA block stays in one GLU half");
+  constexpr int SA_N = BM / 64, SB_N = BNB / 64;  // scale dword DMAs per K-tile (64 rows each)
+  static_assert(SA_N + SB_N == NW, "one scale DMA per wave");
+  static_assert(!GLU || BNO % 64 == 0, "a scale DMA stays in one GLU half");
+  constexpr int A_BYTES = BM * KA, B_BYTES = BNB * KBB;
+  constexpr int STAGE = A_BYTES + B_BYTES + (BM + BNB) * 4;
+  static_assert(STAGE % 1024 == 0, "stage alignment");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+
+  TileInfo t;
+  if (!assign_tile<BM, BNO>(p, t)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int na = min(WM, max(0, (((t.rows + 31) >> 5) - wm + WAVES_M - 1) / WAVES_M));
+
+  // byte strides: codes (A fp8: K bytes a row, B fp4: K/2), scales K/32 bytes a row
+  const int64_t a_ld = p.lda, b_ld = p.ldb, s_ld = p.K / 32;
+  const char* Bb = static_cast<const char*>(p.B) + (int64_t)t.g * p.b_gstride;
+  const char* Sb = reinterpret_cast<const char*>(p.b_scale) + (int64_t)t.g * p.b_scale_gstride;
+  const int ncols = min(BNO, p.N - t.n0);
+  const bool gather = p.a_rows != nullptr;
+  const u32x4 a_desc = gather ? make_desc(p.A, (int)(p.a_nrows * a_ld))
+                              : make_desc(static_cast<const char*>(p.A) + (int64_t)t.row0 * a_ld, (int)(t.rows * a_ld));
+  const u32x4 as_desc = gather ? make_desc(p.a_scale, (int)(p.a_nrows * s_ld))
+                               : make_desc(p.a_scale + (int64_t)t.row0 * s_ld, (int)(t.rows * s_ld));
+  const u32x4 b_desc0 = make_desc(Bb + (int64_t)t.n0 * b_ld, (int)(ncols * b_ld));
+  const u32x4 b_desc1 = GLU ? make_desc(Bb + (int64_t)(p.glu_up_off + t.n0) * b_ld, (int)(ncols * b_ld)) : b_desc0;
+  const u32x4 bs_desc0 = make_desc(Sb + (int64_t)t.n0 * s_ld, (int)(ncols * s_ld));
+  const u32x4 bs_desc1 =
+      GLU ? make_desc(Sb + (int64_t)(p.glu_up_off + t.n0) * s_ld, (int)(ncols * s_ld)) : bs_desc0;
+  const int KT = p.K / kMxK;
+
+  auto a_src = [&](int r) __attribute__((always_inline)) {  // source row of tile row r, or -1
+    if (!gather) return r;
+    const int src = r < t.rows ? p.a_rows[t.row0 + r] : -1;
+    return (src >= 0 && src < p.a_nrows) ? src : -1;
+  };
+  int a_voff[A_PW], b_voff[B_PW];
+  {
+    const int lr = lane / (KA / 16), slot = lane % (KA / 16);
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) {
+      const int r = (wave * A_PW + i) * RPA + lr;
+      const int src = a_src(r);
+      a_voff[i] = src >= 0 ? src * (int)a_ld + ((slot ^ swz<KA>(r)) * 16) : kOutOfRange;
+    }
+  }
+  {
+    const int lr = lane / (KBB / 16), slot = lane % (KBB / 16);
+#pragma unroll
+    for (int i = 0; i < B_PW; ++i) {
+      const int r = (wave * B_PW + i) * RPB + lr;
+      b_voff[i] = (r % BNO) * (int)b_ld + ((slot ^ swz<KBB>(r)) * 16);
+    }
+  }
+  // scale DMA of this wave: A rows [64 w, 64 w + 64) for w < SA_N, else B rows [64 (w - SA_N), ...)
+  u32x4 s_desc;
+  int s_voff;
+  if (wave < SA_N) {
+    const int src = a_src(wave * 64 + lane);
+    s_desc = as_desc;
+    s_voff = src >= 0 ? src * (int)s_ld : kOutOfRange;
+  } else {
+    const int r = (wave - SA_N) * 64 + lane;
+    s_desc = (GLU && (wave - SA_N) * 64 >= BNO) ? bs_desc1 : bs_desc0;
+    s_voff = (r % BNO) * (int)s_ld;
+  }
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
+
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    const unsigned base = lds0 + stage * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) dma16(a_desc, a_voff[i], kt * KA, base + (wave * A_PW + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_PW; ++i) {
+      const bool up = GLU && (wave * B_PW + i) * RPB >= BNO;
+      dma16(up ? b_desc1 : b_desc0, b_voff[i], kt * KBB, base + A_BYTES + (wave * B_PW + i) * 1024);
+    }
+    dma4(s_desc, s_voff, kt * 4, base + A_BYTES + B_BYTES + wave * 256);
+  };
+  constexpr int PER_TILE = A_PW + B_PW + 1;
+  auto wait_tiles_after = [&](int n) __attribute__((always_inline)) {
+    if (NS > 3 && n >= 2) wait_vmcnt<2 * PER_TILE>();
+    else if (NS > 2 && n == 1) wait_vmcnt<PER_TILE>();
+    else wait_vmcnt<0>();
+  };
+
+  f32x16 acc[WM][WN];
+  zero_acc(acc);
+  const int h = lane >> 5, r32 = lane & 31;
+  int foa[2][2], fob[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    foa[s][0] = r32 * KA + (((4 * s + h) ^ swz<KA>(r32)) * 16);
+    foa[s][1] = r32 * KA + (((4 * s + 2 + h) ^ swz<KA>(r32)) * 16);
+    fob[s] = r32 * KBB + (((2 * s + h) ^ swz<KBB>(r32)) * 16);
+  }
+
+  dispatch_na<WM>(na, [&](auto na_c) __attribute__((always_inline)) {
+    constexpr int NA = decltype(na_c)::value;
+    constexpr int NAR = NA > 0 ? NA : 1;
+    auto compute = [&](int stage) __attribute__((always_inline)) {
+      const char* base = smem + stage * STAGE;
+      const uint32_t* sA = reinterpret_cast<const uint32_t*>(base + A_BYTES + B_BYTES);
+      const uint32_t* sB = sA + BM;
+      uint32_t sa[NAR], sb[WN];  // the four block scales of this K-tile, lane half's block in byte 0
+#pragma unroll
+      for (int i = 0; i < NA; ++i) sa[i] = sA[(i * WAVES_M + wm) * 32 + r32] >> (8 * h);
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int ocb = (j % (GLU ? WN / 2 : WN)) * WAVES_N + wn;
+        const int bblk = (GLU && j >= WN / 2) ? BNO / 32 + ocb : ocb;
+        sb[j] = sB[bblk * 32 + r32] >> (8 * h);
+      }
+      uint4 af[2][NAR][2], bf[2][WN];
+      auto load = [&](int s, uint4 (&a)[NAR][2], uint4 (&b)[WN]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+          const char* ab = base + (i * WAVES_M + wm) * 32 * KA;
+          a[i][0] = *reinterpret_cast<const uint4*>(ab + foa[s][0]);
+          a[i][1] = *reinterpret_cast<const uint4*>(ab + foa[s][1]);
+        }
+#pragma unroll
+        for (int j = 0; j < WN; ++j) {
+          const int ocb = (j % (GLU ? WN / 2 : WN)) * WAVES_N + wn;
+          const int bblk = (GLU && j >= WN / 2) ? BNO / 32 + ocb : ocb;
+          b[j] = *reinterpret_cast<const uint4*>(base + A_BYTES + bblk * 32 * KBB + fob[s]);
+        }
+      };
+      load(0, af[0], bf[0]);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (s == 0) load(1, af[1], bf[1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+          const uint4 lo = af[s][i][0], hi = af[s][i][1];
+          const i32x8 av = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          const int sca = (int)((sa[i] >> (16 * s)) & 0xffu);
+#pragma unroll
+          for (int j = 0; j < WN; ++j) {
+            const uint4 bq = bf[s][j];
+            const i32x8 bv = {(int)bq.x, (int)bq.y, (int)bq.z, (int)bq.w, 0, 0, 0, 0};
+            const int scb = (int)((sb[j] >> (16 * s)) & 0xffu);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[i][j], 0, 4, 0, sca, 0, scb);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    const int pre = min(KT, NS - 1);
+    for (int kt = 0; kt < pre; ++kt) issue(kt, kt);
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_tiles_after(min(KT - kt - 1, NS - 2));
+      __syncthreads();
+      if (kt + NS - 1 < KT) issue(kt + NS - 1, (kt + NS - 1) % NS);
+      if (NA > 0) compute(kt % NS);
+    }
+  });
+  constexpr int REGION = NS * STAGE / NW;
+  if (p.N % 8 == 0 && p.ldc % 8 == 0) {
+    __syncthreads();
+    epilogue_staged<uint16_t, uint16_t, WAVES_M, WAVES_N, WM, WN, EPI, REGION>(p, t, acc, wm, wn, lane, na,
+                                                                             smem + wave * REGION);
+    return;
+  }
+  epilogue<uint16_t, WAVES_M, WAVES_N, WM, WN, EPI>(p, t, acc, wm, wn, lane, na);
+}
+
+// ------------------------------------------------------------------------------------------------
 // register pipeline: 128x128 tiles, one K-tile of loads in flight, two padded LDS stages
 // ------------------------------------------------------------------------------------------------
 constexpr int kRowPitch = 144;
@@ -937,6 +1148,24 @@ hipError_t launch_gemm(const GemmArgs& a, int in_dtype, Epi epi, GemmShape shape
   if (in_dtype == LMOE_BF16)
     return shape == GemmShape::Big ? launch_big<uint16_t>(a, epi, s) : launch_small<uint16_t>(a, epi, s);
   return shape == GemmShape::Big ? launch_big<float>(a, epi, s) : launch_small<float>(a, epi, s);
+}
+
+// MX GEMM (bf16 output): A fp8 codes [rows, K] + scales [rows, K/32], B fp4 codes [N, K/2] + scales
+// [N, K/32] per group; lda / ldb / b_gstride / b_scale_gstride in bytes; K a multiple of 128.
+hipError_t launch_gemm_mx(const GemmArgs& a, Epi epi, hipStream_t s) {
+  KernelTimer timer(a.tag ? a.tag : "gemm_mx", s);
+  if ((epi != Epi::Store && epi != Epi::Glu) || a.K % kMxK || a.c_dtype != LMOE_BF16 || a.koff || a.A2 ||
+      a.splits > 1 || a.b_kn || !a.a_scale || !a.b_scale)
+    return hipErrorInvalidValue;
+  const int64_t blocks = grid_blocks<256, 256>(a, epi);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(8 * kWave);
+  if (epi == Epi::Glu)
+    hipLaunchKernelGGL((gemm_mx_kernel<2, 4, 4, 2, kDmaStages, Epi::Glu>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_mx_kernel<2, 4, 4, 2, kDmaStages, Epi::Store>), grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_mtile_prefix(const int32_t* goff, int G, int bm, int32_t* mtile_start, hipStream_t s) {

@@ -10,6 +10,11 @@ allocates buffers and passes pointers.
 fused=True (default): the routed GEMM reads x_lat rows through sorted_token (no permuted copy), and
 the shared experts' down-projection is folded into the up-projection's accumulation (no y_sh).
 fused=False materialises x_perm and y_sh, as separate steps.
+
+mx=True (bf16 layers, [slm] 训练基础设施: MXFP4 weights with MXFP8 activations): the routed experts
+run on MX operands. W1 and W2 are quantised to MXFP4 once, at construction; each forward quantises
+x_lat to MXFP8 (lmoe_mx_quantize) and calls lmoe_grouped_situ_glu_mx, which reads x_lat's codes
+through sorted_token and quantises h itself. Everything else is the bf16 layer.
 """
 from __future__ import annotations
 
@@ -35,8 +40,11 @@ class LatentMoE:
     """One layer instance: weights on the device, per-batch buffers sized for up to ``max_tokens``."""
 
     def __init__(self, cfg, weights: dict, max_tokens: int | None = None, device: str = "cuda",
-                 out_dtype: torch.dtype = torch.float32, fused: bool = True):
+                 out_dtype: torch.dtype = torch.float32, fused: bool = True, mx: bool = False):
         self.cfg = cfg
+        if mx and (cfg.act_dtype != "bf16" or not fused):
+            raise ValueError("MX experts need a bf16 layer on the fused path")
+        self.mx = mx
         self.out_dtype = out_dtype
         self.fused = fused
         self.device = device
@@ -53,6 +61,15 @@ class LatentMoE:
         self.w2s_packed = torch.empty(D, S * Is, dtype=dt, device=device)
         if S > 0:
             C.lmoe_pack_shared(shape, weights["w1s"], weights["w2s"], self.w1s_packed, self.w2s_packed)
+        if mx:
+            self.mx_w = {}
+            for name in ("w1", "w2"):
+                wt = weights[name]
+                G, R, K = wt.shape
+                codes = torch.empty(G, R, K // 2, dtype=torch.uint8, device=device)
+                scales = torch.empty(G, R, K // 32, dtype=torch.uint8, device=device)
+                C.lmoe_mx_quantize(shape, C.LMOE_MX_FP4, G * R, K, wt, codes, scales)
+                self.mx_w[name] = (codes, scales)
         self._bufs = {}
         self._alloc(self.max_tokens)
 
@@ -80,6 +97,11 @@ class LatentMoE:
             "n": torch.empty(T, L, dtype=dt, device=dev),
             "out": torch.empty(T, D, dtype=self.out_dtype, device=dev),
         }
+        if self.mx:
+            b["x_lat_codes"] = torch.empty(T, L, dtype=torch.uint8, device=dev)
+            b["x_lat_scales"] = torch.empty(T, L // 32, dtype=torch.uint8, device=dev)
+            n = C.workspace_bytes(shape, C.LMOE_CALL_GROUPED_GLU_MX)
+            b["ws_glu_mx"] = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
         for name, which in (("ws_route", C.LMOE_CALL_ROUTE), ("ws_permute", C.LMOE_CALL_PERMUTE),
                             ("ws_glu", C.LMOE_CALL_GROUPED_GLU), ("ws_combine", C.LMOE_CALL_COMBINE_NORM_UP)):
             n = C.workspace_bytes(shape, which)
@@ -94,7 +116,8 @@ class LatentMoE:
         if T > self.max_tokens:
             self.max_tokens = T
             self._alloc(T)
-        b = {k: (v[:T] if k in ("scores", "idx", "w", "thresh", "x_lat", "h_s", "n", "out") else v)
+        b = {k: (v[:T] if k in ("scores", "idx", "w", "thresh", "x_lat", "h_s", "n", "out", "x_lat_codes",
+                                "x_lat_scales") else v)
              for k, v in self._bufs.items()}
         b["y_sh"] = self._bufs["y_sh"][:T] if not self.fused else None
         for k in ("sorted_token", "slot_of_pair"):
@@ -113,7 +136,13 @@ class LatentMoE:
         fused = self.fused
         C.lmoe_permute(shape, x, w["w_down"], b["idx"], b["x_lat"], b["offsets"], b["sorted_token"],
                        b["slot_of_pair"], None if fused else b["x_perm"], b["ws_permute"])
-        if fused:
+        if self.mx:
+            C.lmoe_mx_quantize(shape, C.LMOE_MX_FP8, T, L, b["x_lat"], b["x_lat_codes"], b["x_lat_scales"])
+            (w1c, w1s), (w2c, w2s) = self.mx_w["w1"], self.mx_w["w2"]
+            C.lmoe_grouped_situ_glu_mx(shape, E, T * k, L, I, L, b["x_lat_codes"], b["x_lat_scales"], T,
+                                       b["sorted_token"], b["offsets"], w1c, w1s, w2c, w2s, b["h"], b["y"],
+                                       b["ws_glu_mx"])
+        elif fused:
             C.lmoe_grouped_situ_glu(shape, E, T * k, L, I, L, b["x_lat"], b["offsets"], w["w1"], w["w2"], b["h"],
                                     b["y"], b["ws_glu"], a_row_index=b["sorted_token"])
         else:

@@ -19,10 +19,15 @@ Microscaling (MX) ones, read here as:
       elements are one byte each; NaN encodings are never produced.
   RM5 a product of an MX activation row and an MX weight row is the sum over k of
       (X_a p_a)(X_w p_w), evaluated exactly here (float64).
+  RM6 in the routed experts both projections take MX operands: the expert's input rows (x_lat,
+      stored bf16) and its hidden h (stored bf16 after SiTU-GLU) are quantised to MXFP8 along the
+      contraction, W1 and W2 are MXFP4 along theirs; everything else is the bf16 expert.
 """
 from __future__ import annotations
 
 import numpy as np
+
+from . import lmoe_oracle as O
 
 F64 = np.float64
 BLOCK = 32
@@ -124,3 +129,27 @@ def mx_matmul(a_codes, a_scales, w_packed, w_scales) -> np.ndarray:
     a = dequantize(a_codes, a_scales, "fp8")
     w = dequantize(unpack_fp4(w_packed), w_scales, "fp4")
     return a @ w.T
+
+
+def mx_glu_stage(a, w1_codes, w1_scales, beta1: float, beta2: float):
+    """RM6, first projection: a (float64 values of bf16 rows) quantised to MXFP8, times the
+    dequantised FP4 W1 [2I, K] (unpacked codes), SiTU-GLU, stored bf16. Returns (h, a codes, a scales)."""
+    aq, asc = quantize(a, "fp8")
+    w1 = dequantize(w1_codes, w1_scales, "fp4")
+    inter = w1.shape[0] // 2
+    gu = dequantize(aq, asc, "fp8") @ w1.T
+    h = O.store(O.situ(gu[:, :inter], beta1) * O.softcap(gu[:, inter:], beta2), "bf16")
+    return h, aq, asc
+
+
+def mx_down_stage(h, w2_codes, w2_scales):
+    """RM6, second projection: h (float64 values of bf16) quantised to MXFP8 along inter, times the
+    dequantised FP4 W2 [N, I] (unpacked codes), stored bf16."""
+    hq, hs = quantize(h, "fp8")
+    return O.store(dequantize(hq, hs, "fp8") @ dequantize(w2_codes, w2_scales, "fp4").T, "bf16")
+
+
+def mx_expert_ffn(a, w1_codes, w1_scales, w2_codes, w2_scales, beta1: float, beta2: float):
+    """One routed SiTU-GLU expert with MX operands (RM6); returns (h, y)."""
+    h, _, _ = mx_glu_stage(a, w1_codes, w1_scales, beta1, beta2)
+    return h, mx_down_stage(h, w2_codes, w2_scales)

@@ -134,3 +134,31 @@ def test_backward_workspace_and_validation(lib):
     assert lib.lmoe_bwd_router(ctypes.byref(k3), fake, fake, fake, fake, fake, fake, fake, fake, null, null) == \
         C.LMOE_ERR_INVALID_ARGUMENT
     assert lib.lmoe_bwd_up(ctypes.byref(k3), *([fake] * 9), null, 0, null) == C.LMOE_ERR_WORKSPACE
+
+
+def test_mx_workspace_and_validation(lib):
+    """MX calls: the grouped call's workspace (tile list + FP8 h + its scales), argument checks
+    before any launch."""
+    k3 = C.make_shape(CONFIGS["k3_prefill"])
+    rows, inter = 8192 * 16, 512
+    want = 3840 + rows * inter + rows * inter // 32           # (896 + 1) * 4 rounded to 256
+    assert C.workspace_bytes(k3, C.LMOE_CALL_GROUPED_GLU_MX) == want
+    null = None
+    fake = ctypes.c_void_p(0x1000)
+    sh = ctypes.byref(k3)
+    # quantise: unknown format, K not a multiple of 32, rows = 0 is a no-op, misaligned codes
+    assert lib.lmoe_mx_quantize(sh, 5, 4, 64, fake, fake, fake, null) == C.LMOE_ERR_INVALID_ARGUMENT
+    assert lib.lmoe_mx_quantize(sh, C.LMOE_MX_FP8, 4, 48, fake, fake, fake, null) == C.LMOE_ERR_UNSUPPORTED
+    assert lib.lmoe_mx_quantize(sh, C.LMOE_MX_FP4, 0, 64, null, null, null, null) == C.LMOE_OK
+    assert lib.lmoe_mx_quantize(sh, C.LMOE_MX_FP4, 4, 64, fake, ctypes.c_void_p(0x1004), fake, null) == \
+        C.LMOE_ERR_INVALID_ARGUMENT
+    args = [fake] * 2 + [16, null, null] + [fake] * 6
+    # grouped MX: K or inter not a multiple of 128, f32 layers, missing workspace
+    assert lib.lmoe_grouped_situ_glu_mx(sh, 1, 16, 192, 128, 256, *args, null, 0, null) == C.LMOE_ERR_UNSUPPORTED
+    assert lib.lmoe_grouped_situ_glu_mx(sh, 1, 16, 256, 64, 256, *args, null, 0, null) == C.LMOE_ERR_UNSUPPORTED
+    assert lib.lmoe_grouped_situ_glu_mx(sh, 1, 16, 256, 128, 256, *args, null, 0, null) == C.LMOE_ERR_WORKSPACE
+    f32 = C.make_shape(CONFIGS["tiny_f32"])
+    assert lib.lmoe_grouped_situ_glu_mx(ctypes.byref(f32), 1, 16, 256, 128, 256, *args, fake, 1 << 20, null) == \
+        C.LMOE_ERR_UNSUPPORTED
+    assert lib.lmoe_grouped_situ_glu_mx(sh, 2, 16, 256, 128, 256, *args, fake, 1 << 20, null) == \
+        C.LMOE_ERR_INVALID_ARGUMENT                            # several groups need group offsets

@@ -97,3 +97,54 @@ def test_pack_order_and_block_product():
         xw = 2.0 ** (ws[:, b].astype(np.int64) - 127)
         want += np.outer(xa, xw) * (pa @ pw.T)
     np.testing.assert_allclose(got, want, rtol=1e-13, atol=0)
+
+
+def on_grid(rng, rows, K, fmt):
+    """Rows of MX-representable values: random codes and scales with one element per block at a
+    top-binade magnitude, so quantisation returns every value unchanged (and the same scale)."""
+    mags, max_code, emax = M.FORMATS[fmt]
+    codes = rng.integers(0, max_code + 1, (rows, K))
+    top = np.nonzero(mags >= 2.0 ** emax)[0]                  # codes in the largest binade
+    codes[:, ::32] = rng.choice(top, (rows, K // 32))
+    sign = 8 if fmt == "fp4" else 128
+    codes = np.where(rng.random((rows, K)) < 0.5, codes + sign * (codes > 0), codes).astype(np.uint8)
+    scales = rng.integers(120, 134, (rows, K // 32)).astype(np.uint8)
+    return codes, scales, M.dequantize(codes, scales, fmt)
+
+
+def test_mx_glu_stage_on_grid_is_the_bf16_expert():
+    """With operands already on the MX grids the first projection is the (pinned) bf16 expert's:
+    quantisation is the identity there, so h must match situ_glu_ffn's h exactly."""
+    from oracle import lmoe_oracle as O
+    rng = np.random.default_rng(21)
+    I, K, rows = 64, 128, 40
+    w1c, w1s, w1 = on_grid(rng, 2 * I, K, "fp4")
+    ac, asc, a = on_grid(rng, rows, K, "fp8")
+    a = a * 2.0 ** -10                                       # keep the products in a sane range
+    asc = (asc.astype(np.int64) - 10).astype(np.uint8)
+    q, qs = M.quantize(a, "fp8")
+    assert np.array_equal(q, ac) and np.array_equal(qs, asc)
+    h, aq, _ = M.mx_glu_stage(a, w1c, w1s, 4.0, 25.0)
+    h_ref, _ = O.situ_glu_ffn(a, w1, np.zeros((8, I)), 4.0, 25.0, "bf16")
+    assert np.array_equal(aq, ac)
+    assert np.array_equal(h, h_ref)
+
+
+def test_mx_down_stage_brute_force():
+    """Second projection on a tiny case against a scalar loop written from the format fields:
+    y[r, n] = bf16(sum_k 2^(ea-127) fp8(h code) * 2^(ew-127) fp4(w code))."""
+    from oracle import lmoe_oracle as O
+    rng = np.random.default_rng(22)
+    rows, N, I = 3, 5, 64
+    h = O.store(rng.standard_normal((rows, I)) * 3.0, "bf16")
+    w2c, w2s, _ = on_grid(rng, N, I, "fp4")
+    y = M.mx_down_stage(h, w2c, w2s)
+    hq, hs = M.quantize(h, "fp8")
+    for r in range(rows):
+        for n in range(N):
+            acc = 0.0
+            for k in range(I):
+                va = field_value(int(hq[r, k]), 4, 3, 7) * 2.0 ** (int(hs[r, k // 32]) - 127)
+                vw = field_value(int(w2c[n, k]), 2, 1, 1) * 2.0 ** (int(w2s[n, k // 32]) - 127)
+                acc += va * vw
+            assert y[r, n] == O.store(np.array([acc]), "bf16")[0], (r, n)
