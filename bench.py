@@ -6,6 +6,10 @@ combine + RMSNorm + up-projection, and the QB bias update. Inputs are resident i
 timed region. Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload k3_prefill] [--no-cpu-baseline]
+                  [--backward] [--no-mx]
+
+The headline line is the bf16 layer. Under "mx" the same steps are timed with the routed experts on
+MXFP4 weights and MXFP8 activations (a variant with its own numerics, never the headline value).
 """
 from __future__ import annotations
 
@@ -132,6 +136,72 @@ def cpu_baseline(cfg, inp, sample_tokens: int) -> dict:
                       f"{dt:.1f} s"}
 
 
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA (the FP8 x FP4 scaled MFMA runs at this rate)
+MX_KERNELS = ["mx_quantize", "gemm_glu_mx", "gemm_down_mx"]
+
+
+def mx_work(cfg, offsets) -> dict:
+    """Algorithmic work of the MX routed-expert kernels for one forward: FP4 weight slices (0.5 byte
+    per element plus one scale byte per 32) of the experts that received tokens, x_lat's FP8 codes
+    and scales read once, h written in bf16, then read as FP8 codes; y written in bf16."""
+    import numpy as np
+
+    T, L, k, I = cfg.T, cfg.d_latent, cfg.top_k, cfg.inter
+    counts = np.diff(offsets)
+    touched = int((counts > 0).sum())
+    rows = int(offsets[-1])
+    fp4 = lambda n: n / 2 + n / 32  # noqa: E731
+    fp8 = lambda n: n + n / 32      # noqa: E731
+    return {
+        "mx_quantize": ("hbm", 2 * T * L + fp8(T * L) + 2 * rows * I + fp8(rows * I)),
+        "gemm_glu_mx": ("hbm", touched * fp4(2 * I * L) + fp8(T * L) + 2 * rows * I,
+                        2.0 * rows * L * 2 * I),
+        "gemm_down_mx": ("hbm", touched * fp4(L * I) + fp8(rows * I) + 2 * rows * L, 2.0 * rows * I * L),
+    }
+
+
+def mx_steps(cfg, w, x, args, _lib, torch, LatentMoE) -> dict:
+    """Forward steps with the routed experts on MX operands (MXFP4 weights, MXFP8 activations)."""
+    layer = LatentMoE(cfg, w, mx=True)
+
+    def step():
+        layer.forward(x)
+        layer.qb_update()
+
+    for _ in range(max(args.warmup, 2)):
+        step()
+    torch.cuda.synchronize()
+    _lib.profile_reset()
+    _lib.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    _lib.profile_enable(False)
+    _lib.profile_collect()
+    kernels, roof = {}, {}
+    b = layer.forward(x)
+    torch.cuda.synchronize()
+    work = mx_work(cfg, b["offsets"].cpu().numpy())
+    for n in MX_KERNELS:
+        cnt, ms = _lib.profile_get(n)
+        if not cnt:
+            continue
+        kernels[n] = round(ms / args.steps, 4)
+        avg_s = ms / cnt / 1e3
+        gbs = work[n][1] / avg_s / 1e9
+        roof[n] = {"bound": "hbm", "achieved": round(gbs, 1), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                   "avg_launch_ms": round(avg_s * 1e3, 4)}
+        if len(work[n]) > 2:
+            tf = work[n][2] / avg_s / 1e12
+            roof[n].update({"mfma_tflops": round(tf, 1), "mfma_frac_fp8": round(tf / FP8_PEAK_TFLOPS, 4)})
+    ms_step = elapsed / args.steps * 1e3
+    del layer
+    return {"ms_per_step": ms_step, "tokens_per_s": cfg.T / (ms_step / 1e3), "kernels_ms_per_step": kernels,
+            "kernels_roofline": roof}
+
+
 BWD_KERNELS = ["bwd_transpose", "bwd_gemm_dn", "bwd_gemm_dw", "bwd_combine_norm", "bwd_dgamma", "bwd_router_dw",
                "bwd_router_dx", "bwd_gemm_dh", "bwd_gemm_dw_experts", "bwd_gemm_dgu", "bwd_gemm_dx_experts",
                "bwd_unpermute", "bwd_gemm_dx"]
@@ -180,6 +250,8 @@ def main() -> int:
     ap.add_argument("--cpu-sample", type=int, default=256)
     ap.add_argument("--backward", action="store_true",
                     help="also time training steps (forward + backward + bias update) and report them under 'train'")
+    ap.add_argument("--no-mx", action="store_true",
+                    help="skip the forward steps with MX routed experts (reported under 'mx')")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB 5 times (counter calibration)")
     args = ap.parse_args()
@@ -294,6 +366,9 @@ def main() -> int:
     }
     if args.backward:
         out["train"] = train_steps(layer, x, cfg, args, _lib, torch)
+    if not args.no_mx and cfg.act_dtype == "bf16":
+        log("[bench] MX routed experts")
+        out["mx"] = mx_steps(cfg, w, x, args, _lib, torch, LatentMoE)
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on {args.cpu_sample} tokens")
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
