@@ -173,6 +173,8 @@ class LatentMoE:
         Calls, in order: transposed weights, up-projection, combine + norm + routing weights, router,
         routed experts, un-permutation + down-projection, shared experts.
         """
+        if self.mx:
+            raise NotImplementedError("the backward calls take bf16/f32 expert weights, not MX ones")
         cfg, w, dev, dt = self.cfg, self.w, self.device, self.dt
         T = x.shape[0]
         E, k, L, D, I = cfg.n_experts, cfg.top_k, cfg.d_latent, cfg.d_model, cfg.inter
