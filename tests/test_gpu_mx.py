@@ -209,3 +209,46 @@ def test_grouped_mx_k3_sampled():
     order = np.argsort(counts, kind="stable")
     experts = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2])] + list(range(3, 896, 149))))
     check_mx_experts(cfg, inp, layer, b, experts, rows_per_expert=48)
+
+
+def test_grouped_mx_one_group_no_gather():
+    """One group (group_offsets NULL) read without a row gather, a row count that is not a multiple
+    of the 256-row tile, against the oracle's two stages."""
+    cfg = CONFIGS["mid_bf16"]
+    rng = np.random.default_rng(13)
+    rows, K, inter, n_out = 300, 1024, 256, 1024
+    a = O.store(rng.standard_normal((rows, K)), "bf16")
+    w1 = O.store(rng.standard_normal((2 * inter, K)) * K ** -0.5, "bf16")
+    w2 = O.store(rng.standard_normal((n_out, inter)) * inter ** -0.5, "bf16")
+    dev = lambda v: torch.as_tensor(v).to(torch.bfloat16).cuda()  # noqa: E731
+    shape = C.make_shape(cfg, rows)
+    u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device="cuda")  # noqa: E731
+    ac, asc = u8(rows, K), u8(rows, K // 32)
+    w1c, w1s, w2c, w2s = u8(2 * inter, K // 2), u8(2 * inter, K // 32), u8(n_out, inter // 2), u8(n_out, inter // 32)
+    C.lmoe_mx_quantize(shape, C.LMOE_MX_FP8, rows, K, dev(a), ac, asc)
+    C.lmoe_mx_quantize(shape, C.LMOE_MX_FP4, 2 * inter, K, dev(w1), w1c, w1s)
+    C.lmoe_mx_quantize(shape, C.LMOE_MX_FP4, n_out, inter, dev(w2), w2c, w2s)
+    h = torch.empty(rows, inter, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(rows, n_out, dtype=torch.bfloat16, device="cuda")
+    ws = u8(1 << 20)
+    say(f"grouped MX one group: rows={rows} K={K} inter={inter} n_out={n_out}")
+    C.lmoe_grouped_situ_glu_mx(shape, 1, rows, K, inter, n_out, ac, asc, rows, None, None, w1c, w1s, w2c, w2s, h, y,
+                               ws)
+    torch.cuda.synchronize()
+    q1c, q1s = M.quantize(w1, "fp4")
+    q2c, q2s = M.quantize(w2, "fp4")
+    h_ref, _, _ = M.mx_glu_stage(a, q1c, q1s, cfg.beta1, cfg.beta2)
+    e_h = assert_close_rows(host(h), h_ref, "bf16", "h")
+    e_y = assert_close_rows(host(y), M.mx_down_stage(host(h), q2c, q2s), "bf16", "y")
+    say(f"max err/RMS h {e_h:.3e}, y {e_y:.3e}")
+
+
+def test_grouped_mx_k3_decode():
+    """K3 decode (T = 64, 1024 pairs over 896 experts: most groups hold one or two rows)."""
+    cfg = CONFIGS["k3_decode"]
+    say(f"grouped MX K3 decode: T={cfg.T}")
+    inp, layer, b = run_mx_layer(cfg, 0, seed=2)
+    counts = np.diff(b["offsets"].cpu().numpy())
+    live = np.nonzero(counts)[0]
+    experts = sorted(set([int(live[0]), int(live[-1]), int(np.argmax(counts))] + [int(e) for e in live[::60]]))
+    check_mx_experts(cfg, inp, layer, b, experts)
