@@ -64,8 +64,10 @@ size_t mx_glu_ws(int groups, int64_t rows, int inter) {
 
 // Split-K plans of the dense GEMMs behind each call (no split once the batch fills the chip).
 SplitPlan router_plan(const lmoe_shape* sh) {
-  const int D = sh->d_model;
-  return plan_split_k(sh->T, sh->n_experts, sh->act_dtype == LMOE_BF16 ? 3 * D : D, 0, D, esize(sh->act_dtype));
+  const int D = sh->d_model, K = sh->act_dtype == LMOE_BF16 ? 3 * D : D;
+  const SplitPlan small = plan_split_k(sh->T, sh->n_experts, K, 0, D, esize(sh->act_dtype));
+  if (small.splits > 1) return small;
+  return plan_split_k_big(sh->T, sh->n_experts, K, 0, esize(sh->act_dtype));
 }
 SplitPlan down_plan(const lmoe_shape* sh) {
   return plan_split_k(sh->T, sh->d_latent, sh->d_model, 0, sh->d_model, esize(sh->act_dtype));

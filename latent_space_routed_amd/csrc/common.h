@@ -154,10 +154,14 @@ struct GemmArgs {
 // K-split of a dense GEMM on few rows (decode-size batches), so that its register-pipeline tiles
 // occupy every CU; the partial products are then summed by a reduction that applies the epilogue.
 struct SplitPlan {
-  int splits = 1;  // 1 = no split
-  int chunk = 0;   // K elements per split
+  int splits = 1;    // 1 = no split
+  int chunk = 0;     // K elements per split
+  bool big = false;  // splits run on the 256x256 DMA pipeline (else the 128x128 register pipeline)
 };
 SplitPlan plan_split_k(int64_t M, int64_t n_cols, int K1, int K2, int a_kwrap, int esz);
+// Split for a bf16 GEMM whose 256x256 tiles fill between a quarter and all of the CUs: the fewest
+// splits (at most 4) that give every CU a tile, each a whole number of DMA K-tiles of one segment.
+SplitPlan plan_split_k_big(int64_t M, int64_t n_cols, int K1, int K2, int esz);
 size_t split_k_bytes(const SplitPlan& sp, int64_t M, int64_t n_cols);
 // Runs a (dense, non-gathered) GEMM as the planned split plus the reducing epilogue; partials holds
 // split_k_bytes() bytes.

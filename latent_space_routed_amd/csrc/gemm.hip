@@ -313,7 +313,16 @@ __device__ inline void dispatch_na(int na, F&& f) {
 // column) is gathered with 16-bit LDS reads, which the swizzle spreads over distinct banks.
 template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, int NS, int KB, Epi EPI, bool BKN = false>
 __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
-gemm_dma_kernel(GemmArgs p) {
+gemm_dma_kernel(GemmArgs p_in) {
+  GemmArgs p = p_in;
+  int ka0 = 0;  // byte offset inside A's wrapped row where this workgroup's K range starts
+  if (p.splits > 1) {  // split-K (one K segment, no groups): K-chunk blockIdx.y into its own f32 partial
+    const int sp = blockIdx.y;
+    ka0 = (int)(((int64_t)sp * p.K) % p.a_kwrap) * (int)sizeof(TI);
+    p.B = static_cast<const char*>(p.B) + (int64_t)sp * p.K * (int64_t)sizeof(TI);
+    p.K1 = p.K;
+    p.C = static_cast<float*>(p.C) + sp * p.c_split;
+  }
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int BM = WAVES_M * WM * 32;
   constexpr int BNB = WAVES_N * WN * 32;  // rows of B per tile
@@ -395,7 +404,7 @@ gemm_dma_kernel(GemmArgs p) {
   const unsigned lds0 = __builtin_amdgcn_readfirstlane(
       (unsigned)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
 
-  int ka = 0;  // byte offset of the next issued K-tile inside A's (possibly wrapped) row
+  int ka = ka0;  // byte offset of the next issued K-tile inside A's (possibly wrapped) row
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
     const unsigned base = lds0 + stage * STAGE;
     if (!seg2 || kt < KT1) {
@@ -1087,6 +1096,23 @@ SplitPlan plan_split_k(int64_t M, int64_t n_cols, int K1, int K2, int a_kwrap, i
   return best.splits >= 2 ? best : none;
 }
 
+SplitPlan plan_split_k_big(int64_t M, int64_t n_cols, int K1, int K2, int esz) {
+  SplitPlan none;
+  if (esz != 2 || M <= 0 || n_cols <= 0 || n_cols % 4 != 0 || K1 <= 0 || K2 != 0) return none;
+  const int64_t tiles = ceil_div(M, 256) * ceil_div(n_cols, 256);
+  if (tiles >= 256 || tiles < 64) return none;
+  const int gran = kDmaKBytes / esz;  // elements of one DMA K-tile
+  for (int n = (int)ceil_div(256, tiles); n <= 4; ++n) {
+    if (K1 % n || (K1 / n) % gran || K1 / n < 4 * gran) continue;
+    SplitPlan sp;
+    sp.splits = n;
+    sp.chunk = K1 / n;
+    sp.big = true;
+    return sp;
+  }
+  return none;
+}
+
 size_t split_k_bytes(const SplitPlan& sp, int64_t M, int64_t n_cols) {
   return sp.splits > 1 ? (size_t)sp.splits * (size_t)M * (size_t)n_cols * sizeof(float) : 0;
 }
@@ -1108,7 +1134,17 @@ hipError_t launch_gemm_split(const GemmArgs& a, int in_dtype, Epi epi, const Spl
   q.N = n_cols;
   q.col_bias = nullptr;
   q.residual = nullptr;
-  {
+  if (sp.big) {  // the DMA pipeline starts each split at its own offset inside A's wrapped row
+    if (in_dtype != LMOE_BF16 || a.A2 || sp.chunk % (kDmaKBytes / 2)) return hipErrorInvalidValue;
+    KernelTimer timer(a.tag ? a.tag : "gemm", s);
+    const int64_t blocks = grid_blocks<256, 256>(q, Epi::Store);
+    if (blocks <= 0) return hipSuccess;
+    const dim3 grid((unsigned)blocks, (unsigned)sp.splits), block(8 * kWave);
+    hipLaunchKernelGGL((gemm_dma_kernel<uint16_t, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Store>), grid, block, 0, s,
+                       q);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
     KernelTimer timer(a.tag ? a.tag : "gemm", s);
     const int64_t blocks = grid_blocks<128, 128>(q, Epi::Store);
     if (blocks <= 0) return hipSuccess;
