@@ -37,13 +37,13 @@ def k3_weights():
     return _CACHE["inp"], _CACHE["w"]
 
 
-def layer_for(cfg):
+def layer_for(cfg, fused: bool = True):
     inp_w, w = k3_weights()
     inp = dict(inp_w)
     inp["logit_offset"] = logit_offsets(cfg)
     w = dict(w)
     w["logit_offset"] = to_device(inp["logit_offset"], cfg.act_dtype)
-    return inp, LatentMoE(cfg, w)
+    return inp, LatentMoE(cfg, w, fused=fused)
 
 
 def check_sampled_tokens(cfg, inp, b, tokens, what):
@@ -137,6 +137,22 @@ def test_k3_prefill():
     rng = np.random.default_rng(0)
     tokens = np.sort(np.concatenate([rng.choice(cfg.T, 96, replace=False), [0, cfg.T - 1]]))
     check_sampled_tokens(cfg, inp, b, tokens, "k3_prefill")
+
+
+def test_k3_prefill_unfused():
+    """The unfused composition at K3 prefill: x_perm materialised, y_sh stored in f32 and added by
+    the up-projection's epilogue; sampled tokens against the oracle."""
+    cfg = K3
+    inp, layer = layer_for(cfg, fused=False)
+    x_host = token_rows(cfg)
+    inp["x"] = x_host
+    say("[k3_prefill unfused] GPU forward")
+    b = layer.forward(to_device(x_host, cfg.act_dtype))
+    torch.cuda.synchronize()
+    check_routing_all_tokens(cfg, inp, x_host, b, inp["bias"])
+    rng = np.random.default_rng(1)
+    tokens = np.sort(np.concatenate([rng.choice(cfg.T, 32, replace=False), [cfg.T - 1]]))
+    check_sampled_tokens(cfg, inp, b, tokens, "k3_prefill unfused")
 
 
 def test_k3_decode_every_token():

@@ -252,3 +252,46 @@ def test_grouped_mx_k3_decode():
     live = np.nonzero(counts)[0]
     experts = sorted(set([int(live[0]), int(live[-1]), int(np.argmax(counts))] + [int(e) for e in live[::60]]))
     check_mx_experts(cfg, inp, layer, b, experts)
+
+
+def test_grouped_mx_small_dims_and_empty_groups():
+    """The smallest dimensions the call takes (K = inter = 128: one K-tile each), an output width
+    that is not a multiple of the 256-column tile (n_out = 136), and groups that are empty at the
+    start, in the middle and at the end, with rows gathered out of order."""
+    cfg = CONFIGS["mid_bf16"]
+    rng = np.random.default_rng(17)
+    K, inter, n_out, G = 128, 128, 136, 6
+    sizes = np.array([0, 5, 0, 300, 33, 0])
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(offs[-1])
+    a_rows = 100
+    idx = rng.integers(0, a_rows, rows).astype(np.int32)
+    a = O.store(rng.standard_normal((a_rows, K)), "bf16")
+    w1 = O.store(rng.standard_normal((G, 2 * inter, K)) * K ** -0.5, "bf16")
+    w2 = O.store(rng.standard_normal((G, n_out, inter)) * inter ** -0.5, "bf16")
+    dev = lambda v: torch.as_tensor(v).to(torch.bfloat16).cuda()  # noqa: E731
+    u8 = lambda *s: torch.empty(*s, dtype=torch.uint8, device="cuda")  # noqa: E731
+    shape = C.make_shape(cfg, rows)
+    ac, asc = u8(a_rows, K), u8(a_rows, K // 32)
+    w1c, w1s = u8(G, 2 * inter, K // 2), u8(G, 2 * inter, K // 32)
+    w2c, w2s = u8(G, n_out, inter // 2), u8(G, n_out, inter // 32)
+    C.lmoe_mx_quantize(shape, C.LMOE_MX_FP8, a_rows, K, dev(a), ac, asc)
+    C.lmoe_mx_quantize(shape, C.LMOE_MX_FP4, G * 2 * inter, K, dev(w1), w1c, w1s)
+    C.lmoe_mx_quantize(shape, C.LMOE_MX_FP4, G * n_out, inter, dev(w2), w2c, w2s)
+    h = torch.empty(rows, inter, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(rows, n_out, dtype=torch.bfloat16, device="cuda")
+    ws = u8(1 << 20)
+    say(f"grouped MX small dims: groups {sizes.tolist()}, K={K} inter={inter} n_out={n_out}")
+    C.lmoe_grouped_situ_glu_mx(shape, G, rows, K, inter, n_out, ac, asc, a_rows, torch.as_tensor(idx).cuda(),
+                               torch.as_tensor(offs).cuda(), w1c, w1s, w2c, w2s, h, y, ws)
+    torch.cuda.synchronize()
+    hg, yg = host(h), host(y)
+    for g in range(G):
+        lo, hi = int(offs[g]), int(offs[g + 1])
+        if hi == lo:
+            continue
+        q1c, q1s = M.quantize(w1[g], "fp4")
+        q2c, q2s = M.quantize(w2[g], "fp4")
+        h_ref, _, _ = M.mx_glu_stage(a[idx[lo:hi]], q1c, q1s, cfg.beta1, cfg.beta2)
+        assert_close_rows(hg[lo:hi], h_ref, "bf16", f"h group {g}")
+        assert_close_rows(yg[lo:hi], M.mx_down_stage(hg[lo:hi], q2c, q2s), "bf16", f"y group {g}")
