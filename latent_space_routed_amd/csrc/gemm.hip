@@ -103,6 +103,18 @@ __device__ inline void dma16(const u32x4& desc, int voff, int soff, unsigned lds
                : "memory", "m0");
 }
 
+// The same with the non-temporal hint: for operands streamed through once (the routed experts' W1
+// slices), so that they do not displace the gathered latent rows that the other n-tiles of the
+// same expert read again (measured: routed GEMM1 1.54 -> 1.42 ms at K3 prefill; GEMM2, the dense
+// GEMMs and the MX pipeline gain nothing or lose). A template instance of its own, so that the
+// other GEMMs keep their code.
+__device__ inline void dma16_nt(const u32x4& desc, int voff, int soff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(desc), "s"(soff)
+               : "memory", "m0");
+}
+
 // XOR key of the DMA pipeline's LDS layout (rows of KB bytes): the 16-byte slot of chunk c in row r
 // is c ^ swz<KB>(r). A ds_read_b128 is served 16 lanes (256 bytes of banks) at a time, and the 16
 // rows one pass reads then land in 16 distinct 16-byte bank groups.
@@ -311,7 +323,9 @@ __device__ inline void dispatch_na(int na, F&& f) {
 // BKN: B is stored [K, N] (bf16): a K-tile of B is 64 rows of BNB columns, DMA'd row by row into
 // LDS with the 16-byte chunk c of row k at slot c ^ (k % 16); a B fragment (8 consecutive k of one
 // column) is gathered with 16-bit LDS reads, which the swizzle spreads over distinct banks.
-template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, int NS, int KB, Epi EPI, bool BKN = false>
+// NTB: B is streamed through once (the routed experts' W1): its DMA carries the non-temporal hint.
+template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, int NS, int KB, Epi EPI, bool BKN = false,
+          bool NTB = false>
 __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_dma_kernel(GemmArgs p_in) {
   GemmArgs p = p_in;
@@ -413,8 +427,11 @@ gemm_dma_kernel(GemmArgs p_in) {
 #pragma unroll
       for (int i = 0; i < B_PW; ++i) {
         const bool up = GLU && (wave * B_PW + i) * RPD >= BNO;
-        dma16(up ? b_desc1 : b_desc0, b_voff[i], BKN ? kt * (KB / (int)sizeof(TI)) * (int)b_ld : kt * KB,
-              base + A_BYTES + (wave * B_PW + i) * 1024);
+        const int soff = BKN ? kt * (KB / (int)sizeof(TI)) * (int)b_ld : kt * KB;
+        if constexpr (NTB)
+          dma16_nt(up ? b_desc1 : b_desc0, b_voff[i], soff, base + A_BYTES + (wave * B_PW + i) * 1024);
+        else
+          dma16(up ? b_desc1 : b_desc0, b_voff[i], soff, base + A_BYTES + (wave * B_PW + i) * 1024);
       }
       ka += KB;
       if (ka == a_wrap) ka = 0;
@@ -1025,6 +1042,11 @@ hipError_t launch_big(const GemmArgs& a, Epi epi, hipStream_t s) {
     if constexpr (sizeof(TI) == 2)
       hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Store, true>), grid, block, 0, s,
                          a);
+    return hipGetLastError();
+  }
+  if (epi == Epi::Glu && a.goff) {  // routed GEMM1: W1 slices streamed with the non-temporal hint
+    hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Glu, false, true>), grid, block, 0,
+                       s, a);
     return hipGetLastError();
   }
   LMOE_LAUNCH_EPI(gemm_dma_kernel, TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes)
