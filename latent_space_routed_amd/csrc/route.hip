@@ -32,64 +32,104 @@ __global__ void split3_kernel(const float* __restrict__ w, uint16_t* __restrict_
 
 // ------------------------------------------------------------------------------------------------
 // Biased top-k, one wave per token row ([vxz] 02 selection bias; order: descending s + b, equal
-// values to the lower expert index). Lane l holds experts l, l+64, ... in registers; k+1 rounds of
-// (lane-local best, wave arg-max by shuffles) produce the ordered top-(k+1).
+// values to the lower expert index). Lane l holds experts l, l+64, ... in registers as
+// order-preserving integer keys. The (k+1)-th largest key K is found MSB-first, one bit per step,
+// from wave-wide counts (ballots: no cross-lane data movement); the selection is every key above K
+// plus the keys equal to K with the lowest indices; each selected element's place in the order is
+// the count of selected elements ahead of it (broadcast one by one with readlane). The winners meet
+// in LDS so that lane r holds the r-th, and the routing weights are normalised by a fixed-order
+// tree over lanes 0..k-1.
 // ------------------------------------------------------------------------------------------------
-__device__ inline bool better(float va, int ia, float vb, int ib) { return va > vb || (va == vb && ia < ib); }
+__device__ inline uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0;  // -0 and +0 compare equal
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
 
 template <int NPL>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ scores, const float* __restrict__ bias,
                                                    int T, int E, int k, int32_t* __restrict__ idx,
                                                    float* __restrict__ w, float* __restrict__ thresh) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  __shared__ int win_e[4][65];  // ranks 0..k, k <= 64
+  __shared__ uint32_t win_key[4][65];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wv;
+  if (t >= T) return;  // the whole wave leaves together
   const float* row = scores + t * E;
-  float v[NPL];
-  uint32_t taken = 0;  // bit i set: element i of this lane already selected or absent
+  uint32_t key[NPL];
+  uint32_t present = 0;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
+    key[i] = 0;
     if (e < E) {
-      v[i] = row[e] + bias[e];
-    } else {
-      v[i] = -INFINITY;
-      taken |= 1u << i;
+      key[i] = order_key(row[e] + bias[e]);
+      present |= 1u << i;
     }
   }
-  int my_idx = -1;      // lane r keeps the r-th winner
-  float my_s = 0.0f;
-  float vk = 0.0f, vk1 = 0.0f;
-  for (int r = 0; r <= k; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+  const int kk = k + 1;
+  // Wave-wide count of keys >= c: each lane counts its own (vector adds), and the lane counts are
+  // summed bit-slice by bit-slice with ballots, so each step costs log2(NPL) + 1 scalar popcounts
+  // rather than NPL (the scalar unit is shared by the CU's waves).
+  constexpr int CB = NPL <= 2 ? 2 : NPL <= 4 ? 3 : NPL <= 8 ? 4 : NPL <= 16 ? 5 : 6;  // bits of a lane count
+  auto count_ge = [&](uint32_t c) __attribute__((always_inline)) {
+    int own = 0;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + 64 * i;
-      if (!(taken & (1u << i)) && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
-    }
+    for (int i = 0; i < NPL; ++i) own += (((present >> i) & 1u) && key[i] >= c) ? 1 : 0;
+    int total = 0;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const float ov = __shfl_xor(bv, d);
-      const int oi = __shfl_xor(bi, d);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane && bi < E) taken |= 1u << (bi >> 6);
-    if (r < k && lane == r) {
-      my_idx = bi;
-      my_s = row[bi];
-    }
-    if (r == k - 1) vk = bv;
-    if (r == k) vk1 = bv;
+    for (int b = 0; b < CB; ++b) total += __popcll(__ballot((own >> b) & 1)) << b;
+    return total;
+  };
+  uint32_t kth = 0;  // the largest key with at least kk keys >= it: the kk-th largest
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = kth | (1u << b);
+    if (count_ge(cand) >= kk) kth = cand;
   }
-  // sum of the selected unbiased scores: fixed-order tree over lanes 0..k-1
-  float sum = lane < k ? my_s : 0.0f;
+  const int above = kth == 0xffffffffu ? 0 : count_ge(kth + 1);
+  const int need_eq = kk - above;  // >= 1 keys equal to kth, lowest indices first (index = lane + 64 i)
+  const uint64_t lower_lanes = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  uint32_t sel = 0;
+  int eq_before = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const bool p = (present >> i) & 1u;
+    const bool eq = p && key[i] == kth;
+    const uint64_t m = __ballot(eq);
+    if ((p && key[i] > kth) || (eq && eq_before + __popcll(m & lower_lanes) < need_eq)) sel |= 1u << i;
+    eq_before += __popcll(m);
+  }
+  int place[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) place[i] = 0;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    uint64_t m = __ballot((sel >> j) & 1u);
+    while (m) {
+      const int src = __builtin_ctzll(m);
+      m &= m - 1;
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key[j], src);
+      const int ej = src + 64 * j;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const int ei = lane + 64 * i;
+        place[i] += (kj > key[i] || (kj == key[i] && ej < ei)) ? 1 : 0;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NPL; ++i)
+    if ((sel >> i) & 1u) {
+      win_e[wv][place[i]] = lane + 64 * i;
+      win_key[wv][place[i]] = key[i];
+    }
+  __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in issue order
+  const int my_idx = lane < k ? win_e[wv][lane] : 0;
+  const float my_s = lane < k ? row[my_idx] : 0.0f;
+  float sum = my_s;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
   if (lane < k) {
@@ -97,8 +137,8 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ sco
     w[t * k + lane] = my_s / sum;
   }
   if (lane == 0) {
-    thresh[2 * t] = vk;
-    thresh[2 * t + 1] = vk1;
+    thresh[2 * t] = key_value(win_key[wv][k - 1]);
+    thresh[2 * t + 1] = key_value(win_key[wv][k]);
   }
 }
 

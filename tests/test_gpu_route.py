@@ -1,0 +1,63 @@
+"""GPU parity of the biased top-k (lmoe_route) on rows built to stress the ordering rules.
+
+The selection is integer output: indices and the k-th / (k+1)-th biased values are compared bit for
+bit with the oracle's select_topk fed the GPU's own scores, the routing weights within f32
+rounding. Cases: exact ties across experts (duplicated router rows and biases, so equal scores meet
+at the selection boundary), the largest k the library takes (64), an expert count that is not a
+multiple of the 64-lane wave, one expert count past 1024 (NPL = 32 registers per lane), and a row
+count that leaves a partial workgroup.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from latent_space_routed_amd import _lib as C
+from oracle import lmoe_oracle as O
+from workloads import CONFIGS
+
+from .gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (T, D, E, k, duplicate group size of router rows)
+    "ties_E128_k8": (301, 256, 128, 8, 4),
+    "k64_E128": (130, 256, 128, 64, 1),
+    "E100_k7_ties": (77, 128, 100, 7, 5),
+    "E2048_k16": (64, 128, 2048, 16, 2),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_route_topk_ordering(name):
+    T, D, E, k, dup = CASES[name]
+    cfg = replace(CONFIGS["mid_bf16"], T=T, d_model=D, n_experts=E, top_k=k)
+    rng = np.random.default_rng(31)
+    base = (rng.standard_normal((-(-E // dup), D)) * D ** -0.5).astype(np.float32)
+    w_router = np.repeat(base, dup, axis=0)[:E].copy()
+    bias = np.repeat(rng.choice([0.0, 0.01, -0.02], -(-E // dup)).astype(np.float32), dup)[:E].copy()
+    x = O.store(rng.standard_normal((T, D)), "bf16")
+    dev = "cuda"
+    xd = torch.as_tensor(x).to(torch.bfloat16).to(dev)
+    shape = C.make_shape(cfg, T)
+    scores = torch.empty(T, E, dtype=torch.float32, device=dev)
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    wts = torch.empty(T, k, dtype=torch.float32, device=dev)
+    thr = torch.empty(T, 2, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(C.workspace_bytes(shape, C.LMOE_CALL_ROUTE), 256), dtype=torch.uint8, device=dev)
+    say(f"route {name}: T={T} E={E} k={k} duplicate rows x{dup}")
+    C.lmoe_route(shape, xd, torch.as_tensor(w_router).to(dev), torch.as_tensor(bias).to(dev), None, scores, idx, wts,
+                 thr, ws)
+    torch.cuda.synchronize()
+    s = scores.cpu().numpy()
+    ref_idx, ref_w, ref_thr = O.select_topk(s, bias, k)
+    if dup > 1:  # the case really has ties at the boundary
+        sb = s + bias[None, :]
+        ties = np.sum(sb == ref_thr[:, :1], axis=1) > 1
+        say(f"rows with a tie at the k-th value: {int(ties.sum())} of {T}")
+        assert ties.any()
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_array_equal(thr.cpu().numpy(), ref_thr)
+    np.testing.assert_allclose(wts.cpu().numpy(), ref_w, rtol=3e-7, atol=0)
