@@ -80,6 +80,7 @@ def kernel_work(cfg, offsets, fused: bool = True) -> dict:
         "qb_hist": ("hbm", T * E * 4 + E * 4 + T * 8 + T * k * 4 + E * NB * 4 * 2),
         "gemm_down": ("mfma", 2.0 * T * D * L),
         "perm_count": ("hbm", T * k * 4),
+        "perm_scan": ("hbm", -(-T // 256) * E * 4 * 2 + (E + 1) * 4),
         "perm_scatter": ("hbm", T * k * 12),
         "gemm_glu_grouped": ("hbm", glu_b),
         "gemm_down_grouped": ("hbm", touched * L * I * esz + rows * (I + L) * esz),
@@ -189,12 +190,12 @@ def mx_steps(cfg, w, x, args, _lib, torch, LatentMoE) -> dict:
         if not cnt:
             continue
         kernels[n] = round(ms / args.steps, 4)
-        avg_s = ms / cnt / 1e3
-        gbs = work[n][1] / avg_s / 1e9
+        step_s = ms / args.steps / 1e3  # the work is per step (the quantize kernel runs twice a step)
+        gbs = work[n][1] / step_s / 1e9
         roof[n] = {"bound": "hbm", "achieved": round(gbs, 1), "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                   "avg_launch_ms": round(avg_s * 1e3, 4)}
+                   "launches_per_step": round(cnt / args.steps, 2), "avg_launch_ms": round(ms / cnt, 4)}
         if len(work[n]) > 2:
-            tf = work[n][2] / avg_s / 1e12
+            tf = work[n][2] / step_s / 1e12
             roof[n].update({"mfma_tflops": round(tf, 1), "mfma_frac_fp8": round(tf / FP8_PEAK_TFLOPS, 4)})
     ms_step = elapsed / args.steps * 1e3
     del layer
@@ -247,7 +248,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="k3_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=256)
+    ap.add_argument("--cpu-sample", type=int, default=384)
     ap.add_argument("--backward", action="store_true",
                     help="also time training steps (forward + backward + bias update) and report them under 'train'")
     ap.add_argument("--no-mx", action="store_true",

@@ -33,12 +33,18 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ c
                                                           int32_t* __restrict__ offsets) {
   extern __shared__ int32_t tot[];  // [E]
   __shared__ int32_t wsum[16];
+  constexpr int B = 16;  // chunk counts loaded together, so that their latencies overlap
   for (int e = threadIdx.x; e < E; e += 1024) {
     int32_t run = 0;
-    for (int c = 0; c < chunks; ++c) {
-      const int32_t v = cc[(int64_t)c * E + e];
-      cc[(int64_t)c * E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < chunks; c0 += B) {
+      int32_t v[B];
+#pragma unroll
+      for (int i = 0; i < B; ++i) v[i] = c0 + i < chunks ? cc[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        if (c0 + i < chunks) cc[(int64_t)(c0 + i) * E + e] = run;
+        run += v[i];
+      }
     }
     tot[e] = run;
   }

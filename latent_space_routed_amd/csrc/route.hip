@@ -33,12 +33,22 @@ __global__ void split3_kernel(const float* __restrict__ w, uint16_t* __restrict_
 // ------------------------------------------------------------------------------------------------
 // Biased top-k, one wave per token row ([vxz] 02 selection bias; order: descending s + b, equal
 // values to the lower expert index). Lane l holds experts l, l+64, ... in registers as
-// order-preserving integer keys. The (k+1)-th largest key K is found MSB-first, one bit per step,
-// from wave-wide counts (ballots: no cross-lane data movement); the selection is every key above K
-// plus the keys equal to K with the lowest indices; each selected element's place in the order is
-// the count of selected elements ahead of it (broadcast one by one with readlane). The winners meet
-// in LDS so that lane r holds the r-th, and the routing weights are normalised by a fixed-order
-// tree over lanes 0..k-1.
+// order-preserving integer keys.
+//
+// Candidate pass: the (k+1)-th largest of the 64 lane maxima is a lower bound t0 of the (k+1)-th
+// largest key (k+1 distinct keys, one per lane, reach it), so the k+1 winners are among the keys
+// >= t0. For scores without mass ties these are a few dozen; when at most 64 they are compacted
+// one per lane through LDS and each one's place in the order is counted directly against the
+// others (keys compared, then indices). Radix select on the lane maxima costs one compare per bit
+// instead of one per key.
+//
+// Exact pass (more than 64 candidates, e.g. many equal scores): the (k+1)-th largest key K is found
+// MSB-first, one bit per step, from wave-wide counts (ballots: no cross-lane data movement); the
+// selection is every key above K plus the keys equal to K with the lowest indices; each selected
+// element's place in the order is the count of selected elements ahead of it.
+//
+// Either way the winners meet in LDS so that lane r holds the r-th, and the routing weights are
+// normalised by a fixed-order tree over lanes 0..k-1.
 // ------------------------------------------------------------------------------------------------
 __device__ inline uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -55,6 +65,8 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ sco
                                                    float* __restrict__ w, float* __restrict__ thresh) {
   __shared__ int win_e[4][65];  // ranks 0..k, k <= 64
   __shared__ uint32_t win_key[4][65];
+  __shared__ int cand_e[4][64];
+  __shared__ uint32_t cand_key[4][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 4 + wv;
   if (t >= T) return;  // the whole wave leaves together
@@ -71,62 +83,108 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ sco
     }
   }
   const int kk = k + 1;
-  // Wave-wide count of keys >= c: each lane counts its own (vector adds), and the lane counts are
-  // summed bit-slice by bit-slice with ballots, so each step costs log2(NPL) + 1 scalar popcounts
-  // rather than NPL (the scalar unit is shared by the CU's waves).
-  constexpr int CB = NPL <= 2 ? 2 : NPL <= 4 ? 3 : NPL <= 8 ? 4 : NPL <= 16 ? 5 : 6;  // bits of a lane count
-  auto count_ge = [&](uint32_t c) __attribute__((always_inline)) {
-    int own = 0;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) own += (((present >> i) & 1u) && key[i] >= c) ? 1 : 0;
+  const uint64_t lower_lanes = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  // Wave-wide sum of per-lane counts (each below 2^CB): the lane counts are summed bit-slice by
+  // bit-slice with ballots, log2(NPL) + 1 scalar popcounts rather than NPL.
+  constexpr int CB = NPL <= 2 ? 2 : NPL <= 4 ? 3 : NPL <= 8 ? 4 : NPL <= 16 ? 5 : 6;
+  auto wave_sum = [&](int own) __attribute__((always_inline)) {
     int total = 0;
 #pragma unroll
     for (int b = 0; b < CB; ++b) total += __popcll(__ballot((own >> b) & 1)) << b;
     return total;
   };
-  uint32_t kth = 0;  // the largest key with at least kk keys >= it: the kk-th largest
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = kth | (1u << b);
-    if (count_ge(cand) >= kk) kth = cand;
-  }
-  const int above = kth == 0xffffffffu ? 0 : count_ge(kth + 1);
-  const int need_eq = kk - above;  // >= 1 keys equal to kth, lowest indices first (index = lane + 64 i)
-  const uint64_t lower_lanes = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  uint32_t sel = 0;
-  int eq_before = 0;
+  auto count_ge = [&](uint32_t c) __attribute__((always_inline)) {
+    int own = 0;
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const bool p = (present >> i) & 1u;
-    const bool eq = p && key[i] == kth;
-    const uint64_t m = __ballot(eq);
-    if ((p && key[i] > kth) || (eq && eq_before + __popcll(m & lower_lanes) < need_eq)) sel |= 1u << i;
-    eq_before += __popcll(m);
-  }
-  int place[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) place[i] = 0;
-#pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    uint64_t m = __ballot((sel >> j) & 1u);
-    while (m) {
-      const int src = __builtin_ctzll(m);
-      m &= m - 1;
-      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key[j], src);
-      const int ej = src + 64 * j;
-#pragma unroll
-      for (int i = 0; i < NPL; ++i) {
-        const int ei = lane + 64 * i;
-        place[i] += (kj > key[i] || (kj == key[i] && ej < ei)) ? 1 : 0;
-      }
-    }
-  }
+    for (int i = 0; i < NPL; ++i) own += (((present >> i) & 1u) && key[i] >= c) ? 1 : 0;
+    return wave_sum(own);
+  };
+
+  // candidate pass
+  uint32_t lmax = 0;
 #pragma unroll
   for (int i = 0; i < NPL; ++i)
-    if ((sel >> i) & 1u) {
-      win_e[wv][place[i]] = lane + 64 * i;
-      win_key[wv][place[i]] = key[i];
+    if ((present >> i) & 1u) lmax = key[i] > lmax ? key[i] : lmax;
+  const bool voter = present != 0;
+  uint32_t t0 = 0;  // the kk-th largest lane maximum (0 when fewer than kk lanes hold experts)
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = t0 | (1u << b);
+    if (__popcll(__ballot(voter && lmax >= cand)) >= kk) t0 = cand;
+  }
+  int own = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) own += (((present >> i) & 1u) && key[i] >= t0) ? 1 : 0;
+  const int n_cand = wave_sum(own);
+  if (n_cand <= 64) {
+    int pos = 0;  // exclusive prefix of the lane counts
+#pragma unroll
+    for (int b = 0; b < CB; ++b) pos += __popcll(__ballot((own >> b) & 1) & lower_lanes) << b;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if (((present >> i) & 1u) && key[i] >= t0) {
+        cand_key[wv][pos] = key[i];
+        cand_e[wv][pos] = lane + 64 * i;
+        ++pos;
+      }
+    __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in issue order
+    const bool have = lane < n_cand;
+    const uint32_t ck = have ? cand_key[wv][lane] : 0u;
+    const int ce = have ? cand_e[wv][lane] : 0;
+    int place = 0;
+    for (int j = 0; j < n_cand; ++j) {
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)ck, j);
+      const int ej = __builtin_amdgcn_readlane(ce, j);
+      place += (kj > ck || (kj == ck && ej < ce)) ? 1 : 0;
     }
-  __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in issue order
+    if (have && place < kk) {
+      win_e[wv][place] = ce;
+      win_key[wv][place] = ck;
+    }
+  } else {
+    // exact pass
+    uint32_t kth = 0;  // the largest key with at least kk keys >= it: the kk-th largest
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = kth | (1u << b);
+      if (count_ge(cand) >= kk) kth = cand;
+    }
+    const int above = kth == 0xffffffffu ? 0 : count_ge(kth + 1);
+    const int need_eq = kk - above;  // >= 1 keys equal to kth, lowest indices first (index = lane + 64 i)
+    uint32_t sel = 0;
+    int eq_before = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const bool p = (present >> i) & 1u;
+      const bool eq = p && key[i] == kth;
+      const uint64_t m = __ballot(eq);
+      if ((p && key[i] > kth) || (eq && eq_before + __popcll(m & lower_lanes) < need_eq)) sel |= 1u << i;
+      eq_before += __popcll(m);
+    }
+    int place[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) place[i] = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      uint64_t m = __ballot((sel >> j) & 1u);
+      while (m) {
+        const int src = __builtin_ctzll(m);
+        m &= m - 1;
+        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key[j], src);
+        const int ej = src + 64 * j;
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+          const int ei = lane + 64 * i;
+          place[i] += (kj > key[i] || (kj == key[i] && ej < ei)) ? 1 : 0;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+      if ((sel >> i) & 1u) {
+        win_e[wv][place[i]] = lane + 64 * i;
+        win_key[wv][place[i]] = key[i];
+      }
+  }
+  __builtin_amdgcn_wave_barrier();
   const int my_idx = lane < k ? win_e[wv][lane] : 0;
   const float my_s = lane < k ? row[my_idx] : 0.0f;
   float sum = my_s;
@@ -143,48 +201,83 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ sco
 }
 
 // ------------------------------------------------------------------------------------------------
-// QB histogram ([tahou] 负载均衡优化: map to 0..1 and bin). A workgroup owns a slice of EB experts
-// and a chunk of tokens; its [EB, NB] counters live in LDS and are flushed with one integer
-// atomic per non-zero bin. Selection of e by t is decided from the row's k-th value v_k and the
-// k-th expert index e_k (the order is value desc, index asc): e is selected iff
-// s_hat > v_k, or s_hat == v_k and e <= e_k.
+// QB histogram ([tahou] 负载均衡优化: map to 0..1 and bin). A workgroup owns a slice of EB
+// experts for every token: its [EB, NB] counters live in LDS and are added to the caller's
+// histogram with plain read-add-writes (no other workgroup touches those bins), so the result is
+// exact and independent of scheduling. Thread i handles tokens i, i + 512, ...: per token it reads
+// the slice's EB scores (one vector load when the row layout allows), the row's thresholds and
+// its k-th expert index, U tokens at a time so that the loads overlap. Slices are numbered so that
+// the slices on one XCD (workgroup w runs on XCD w % 8) are contiguous experts, and the cache lines
+// of a score row that they share are fetched into that XCD's L2 once.
+// Selection of e by t is decided from the row's k-th value v_k and the k-th expert index e_k (the
+// order is value desc, index asc): e is selected iff s_hat > v_k, or s_hat == v_k and e <= e_k.
 // ------------------------------------------------------------------------------------------------
 constexpr int kHistThreads = 512;
 constexpr int kHistLdsBytes = 128 * 1024;
+constexpr int kHistUnroll = 4;
 
+__device__ inline int xcd_contiguous(int w, int n) {  // bijection on [0, n): XCD x gets a contiguous run
+  const int x = w % kXcds, m = w / kXcds, q = n / kXcds, r = n % kXcds;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + m;
+}
+
+template <int EB, bool VEC>
 __global__ void __launch_bounds__(kHistThreads)
     qb_hist_kernel(const float* __restrict__ scores, const float* __restrict__ bias, const int32_t* __restrict__ idx,
-                   const float* __restrict__ thresh, int T, int E, int k, int nb, int eb, int tchunk,
-                   uint32_t* __restrict__ hist) {
-  extern __shared__ uint32_t cnt[];  // [eb][nb]
-  const int e0 = blockIdx.x * eb;
-  const int t0 = blockIdx.y * tchunk;
-  const int t1 = min(T, t0 + tchunk);
-  for (int i = threadIdx.x; i < eb * nb; i += kHistThreads) cnt[i] = 0;
+                   const float* __restrict__ thresh, int T, int E, int k, int nb, uint32_t* __restrict__ hist) {
+  extern __shared__ uint32_t cnt[];  // [EB][nb]
+  const int e0 = xcd_contiguous(blockIdx.x, gridDim.x) * EB;
+  for (int i = threadIdx.x; i < EB * nb; i += kHistThreads) cnt[i] = 0;
   __syncthreads();
-  // threads cover (token lane, expert lane) = (tid / eb, tid % eb); eb divides 512
-  const int el = threadIdx.x % eb, tl = threadIdx.x / eb, tstep = kHistThreads / eb;
-  const int e = e0 + el;
-  if (e < E) {
-    const float be = bias[e];
-    const float fnb = (float)nb;
-    for (int t = t0 + tl; t < t1; t += tstep) {
-      const float vk = thresh[2 * (int64_t)t], vk1 = thresh[2 * (int64_t)t + 1];
-      const int ek = idx[(int64_t)t * k + k - 1];
-      const float sh = __fadd_rn(scores[(int64_t)t * E + e], be);
-      const bool sel = sh > vk || (sh == vk && e <= ek);
-      const float m = __fsub_rn(sh, sel ? vk1 : vk);
-      float u = __fmul_rn(__fadd_rn(m, 1.0f), 0.5f);
-      u = fminf(fmaxf(u, 0.0f), 1.0f);
-      const int b = min(nb - 1, (int)floorf(__fmul_rn(u, fnb)));
-      atomicAdd(&cnt[el * nb + b], 1u);
+  float be[EB];
+#pragma unroll
+  for (int j = 0; j < EB; ++j) be[j] = e0 + j < E ? bias[e0 + j] : 0.0f;
+  const float fnb = (float)nb;
+  for (int tb = 0; tb < T; tb += kHistThreads * kHistUnroll) {
+    float s[kHistUnroll][EB], vk[kHistUnroll], vk1[kHistUnroll];
+    int ek[kHistUnroll];
+#pragma unroll
+    for (int u = 0; u < kHistUnroll; ++u) {
+      const int t = tb + u * kHistThreads + threadIdx.x;
+      const bool live = t < T;
+      const int64_t tc = live ? t : 0;
+      const float* row = scores + tc * E + e0;
+      if constexpr (VEC && EB == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(row);
+        s[u][0] = v.x, s[u][1] = v.y, s[u][2] = v.z, s[u][3] = v.w;
+      } else if constexpr (VEC && EB == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(row);
+        s[u][0] = v.x, s[u][1] = v.y;
+      } else {
+#pragma unroll
+        for (int j = 0; j < EB; ++j) s[u][j] = e0 + j < E ? row[j] : 0.0f;
+      }
+      vk[u] = thresh[2 * tc];
+      vk1[u] = thresh[2 * tc + 1];
+      ek[u] = live ? idx[tc * k + k - 1] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kHistUnroll; ++u) {
+      if (ek[u] < 0) continue;  // past the last token
+#pragma unroll
+      for (int j = 0; j < EB; ++j) {
+        const int e = e0 + j;
+        if (e >= E) continue;
+        const float sh = __fadd_rn(s[u][j], be[j]);
+        const bool sel = sh > vk[u] || (sh == vk[u] && e <= ek[u]);
+        const float m = __fsub_rn(sh, sel ? vk1[u] : vk[u]);
+        float uu = __fmul_rn(__fadd_rn(m, 1.0f), 0.5f);
+        uu = fminf(fmaxf(uu, 0.0f), 1.0f);
+        const int b = min(nb - 1, (int)floorf(__fmul_rn(uu, fnb)));
+        atomicAdd(&cnt[j * nb + b], 1u);
+      }
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < eb * nb; i += kHistThreads) {
+  for (int i = threadIdx.x; i < EB * nb; i += kHistThreads) {
     const uint32_t c = cnt[i];
-    const int ee = e0 + i / nb;
-    if (c != 0 && ee < E) atomicAdd(&hist[(int64_t)ee * nb + i % nb], c);
+    const int e = e0 + i / nb;
+    if (c != 0 && e < E) hist[(int64_t)e * nb + i % nb] += c;
   }
 }
 
@@ -259,26 +352,35 @@ hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int
   return hipGetLastError();
 }
 
+template <int EB, bool VEC>
+hipError_t launch_qb_hist_t(const float* scores, const float* bias, const int32_t* idx, const float* thresh, int T,
+                            int E, int k, int nb, uint32_t* hist, hipStream_t s) {
+  static bool attr_set = false;  // the LDS limit is a property of the function: set once, before any launch
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute((const void*)qb_hist_kernel<EB, VEC>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kHistLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((qb_hist_kernel<EB, VEC>), dim3((unsigned)ceil_div(E, EB)), dim3(kHistThreads),
+                     (size_t)EB * nb * 4, s, scores, bias, idx, thresh, T, E, k, nb, hist);
+  return hipGetLastError();
+}
+
 hipError_t launch_qb_hist(const float* scores, const float* bias, const int32_t* idx, const float* thresh, int T,
                           int E, int k, int nb, uint32_t* hist, hipStream_t s) {
   KernelTimer timer("qb_hist", s);
-  // experts per slice: a power of two dividing 512, with eb * nb counters fitting the LDS budget
-  int eb = 32;
-  while (eb > 1 && (int64_t)eb * nb * 4 > kHistLdsBytes) eb >>= 1;
-  if ((int64_t)eb * nb * 4 > kHistLdsBytes) return hipErrorInvalidValue;
-  const int slices = (int)ceil_div(E, eb);
-  const int want_chunks = (int)hmax(1, ceil_div(512, slices));
-  const int tchunk = (int)hmax(64, ceil_div(T, want_chunks));
-  const int chunks = (int)ceil_div(T, tchunk);
-  const size_t lds = (size_t)eb * nb * 4;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute((const void*)qb_hist_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kHistLdsBytes);
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(qb_hist_kernel, dim3(slices, chunks), dim3(kHistThreads), lds, s, scores, bias, idx, thresh, T,
-                     E, k, nb, eb, tchunk, hist);
-  return hipGetLastError();
+  // experts per workgroup: the most that still give 256 workgroups (one per CU), within the LDS
+  // budget; vector loads of a slice need E a multiple of EB and an aligned score matrix
+  auto fits = [&](int eb) { return (int64_t)eb * nb * 4 <= kHistLdsBytes; };
+  const int eb = (fits(4) && ceil_div(E, 4) >= 256) ? 4 : (fits(2) && ceil_div(E, 2) >= 256) ? 2 : 1;
+  if (!fits(eb)) return hipErrorInvalidValue;
+  const bool vec = E % eb == 0 && reinterpret_cast<uintptr_t>(scores) % (4 * eb) == 0;
+  if (eb == 4) return vec ? launch_qb_hist_t<4, true>(scores, bias, idx, thresh, T, E, k, nb, hist, s)
+                          : launch_qb_hist_t<4, false>(scores, bias, idx, thresh, T, E, k, nb, hist, s);
+  if (eb == 2) return vec ? launch_qb_hist_t<2, true>(scores, bias, idx, thresh, T, E, k, nb, hist, s)
+                          : launch_qb_hist_t<2, false>(scores, bias, idx, thresh, T, E, k, nb, hist, s);
+  return launch_qb_hist_t<1, false>(scores, bias, idx, thresh, T, E, k, nb, hist, s);
 }
 
 hipError_t launch_qb_update(uint32_t* hist, int E, int k, int nb, int64_t n_acc, float* bias, hipStream_t s) {

@@ -5,7 +5,13 @@ bit with the oracle's select_topk fed the GPU's own scores, the routing weights 
 rounding. Cases: exact ties across experts (duplicated router rows and biases, so equal scores meet
 at the selection boundary), the largest k the library takes (64), an expert count that is not a
 multiple of the 64-lane wave, one expert count past 1024 (NPL = 32 registers per lane), and a row
-count that leaves a partial workgroup.
+count that leaves a partial workgroup. Rows whose winners are all among the keys at or above the
+(k+1)-th largest lane maximum take the kernel's candidate pass, the others (k = 64 at E = 128, mass
+ties) its exact pass; both are covered here.
+
+The QB histogram of the same rows is compared bin for bin with the oracle's: expert counts that
+give the kernel one, two or four experts per workgroup, with and without vector loads of a slice
+(E odd), and bin counts from 2 to 4096.
 """
 from dataclasses import replace
 
@@ -27,13 +33,17 @@ CASES = {
     "k64_E128": (130, 256, 128, 64, 1),
     "E100_k7_ties": (77, 128, 100, 7, 5),
     "E2048_k16": (64, 128, 2048, 16, 2),
+    "E1001_k16": (200, 128, 1001, 16, 1),
+    "E896_k16": (1030, 128, 896, 16, 1),
 }
+HIST_BINS = {"ties_E128_k8": 2, "k64_E128": 1000, "E100_k7_ties": 37, "E2048_k16": 4096, "E1001_k16": 1000,
+             "E896_k16": 1000}
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_route_topk_ordering(name):
     T, D, E, k, dup = CASES[name]
-    cfg = replace(CONFIGS["mid_bf16"], T=T, d_model=D, n_experts=E, top_k=k)
+    cfg = replace(CONFIGS["mid_bf16"], T=T, d_model=D, n_experts=E, top_k=k, n_bins=HIST_BINS[name])
     rng = np.random.default_rng(31)
     base = (rng.standard_normal((-(-E // dup), D)) * D ** -0.5).astype(np.float32)
     w_router = np.repeat(base, dup, axis=0)[:E].copy()
@@ -61,3 +71,8 @@ def test_route_topk_ordering(name):
     np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
     np.testing.assert_array_equal(thr.cpu().numpy(), ref_thr)
     np.testing.assert_allclose(wts.cpu().numpy(), ref_w, rtol=3e-7, atol=0)
+    hist = torch.zeros(E, cfg.n_bins, dtype=torch.int32, device=dev)
+    C.lmoe_qb_histogram(shape, scores, torch.as_tensor(bias).to(dev), idx, thr, hist)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(hist.cpu().numpy().view(np.uint32),
+                                  O.qb_histogram(s, bias, ref_idx, ref_thr, cfg.n_bins))
