@@ -57,11 +57,18 @@ __global__ void __launch_bounds__(256) combine_norm_kernel(const T* __restrict__
   for (int i = 0; i < CPL; ++i)
 #pragma unroll
     for (int v = 0; v < V; ++v) z[i][v] = 0.0f;
+  // the token's slots and weights are loaded once, lane j holding pair j (k <= 64), and read back
+  // as wave-uniform values, so no load of a y row waits on a load of its slot
+  const int32_t my_slot = lane < k ? slot_of_pair[t * k + lane] : -1;
+  const float my_w = lane < k ? w[t * k + lane] : 0.0f;
   // two rows in flight per step; the sum still runs in rank order j = 0, 1, 2, ...
   for (int j = 0; j < k; j += 2) {
     const bool two = j + 1 < k;
-    const int32_t s0 = slot_of_pair[t * k + j], s1 = two ? slot_of_pair[t * k + j + 1] : -1;
-    const float w0 = w[t * k + j], w1 = two ? w[t * k + j + 1] : 0.0f;
+    const int32_t s0 = __builtin_amdgcn_readlane(my_slot, j);
+    const int32_t s1 = two ? __builtin_amdgcn_readlane(my_slot, j + 1) : -1;
+    const float w0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), j));
+    const float w1 = two ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), j + 1))
+                         : 0.0f;
     uint4 r0[CPL], r1[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
@@ -113,12 +120,16 @@ hipError_t launch_t(const void* y, const int32_t* sp, const float* w, const floa
   const dim3 grid((unsigned)ceil_div(T_, 4)), block(256);
   const T* yy = static_cast<const T*>(y);
   T* nn = static_cast<T*>(n);
-  if (cpl <= 1) hipLaunchKernelGGL((combine_norm_kernel<T, 1>), grid, block, 0, s, yy, sp, w, gamma, T_, k, L, eps, nn);
-  else if (cpl <= 2) hipLaunchKernelGGL((combine_norm_kernel<T, 2>), grid, block, 0, s, yy, sp, w, gamma, T_, k, L, eps, nn);
-  else if (cpl <= 4) hipLaunchKernelGGL((combine_norm_kernel<T, 4>), grid, block, 0, s, yy, sp, w, gamma, T_, k, L, eps, nn);
-  else if (cpl <= 8) hipLaunchKernelGGL((combine_norm_kernel<T, 8>), grid, block, 0, s, yy, sp, w, gamma, T_, k, L, eps, nn);
-  else if (cpl <= 16) hipLaunchKernelGGL((combine_norm_kernel<T, 16>), grid, block, 0, s, yy, sp, w, gamma, T_, k, L, eps, nn);
-  else return hipErrorInvalidValue;
+#define LMOE_COMBINE_CASE(C) \
+  case C: hipLaunchKernelGGL((combine_norm_kernel<T, C>), grid, block, 0, s, yy, sp, w, gamma, T_, k, L, eps, nn); break;
+  switch (cpl) {  // one instance per chunk count, so no lane carries a dead chunk's registers
+    LMOE_COMBINE_CASE(1) LMOE_COMBINE_CASE(2) LMOE_COMBINE_CASE(3) LMOE_COMBINE_CASE(4)
+    LMOE_COMBINE_CASE(5) LMOE_COMBINE_CASE(6) LMOE_COMBINE_CASE(7) LMOE_COMBINE_CASE(8)
+    LMOE_COMBINE_CASE(9) LMOE_COMBINE_CASE(10) LMOE_COMBINE_CASE(11) LMOE_COMBINE_CASE(12)
+    LMOE_COMBINE_CASE(13) LMOE_COMBINE_CASE(14) LMOE_COMBINE_CASE(15) LMOE_COMBINE_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef LMOE_COMBINE_CASE
   return hipGetLastError();
 }
 

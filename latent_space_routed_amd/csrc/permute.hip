@@ -86,26 +86,42 @@ __global__ void __launch_bounds__(kPermChunk) perm_scatter_kernel(const int32_t*
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * kPermChunk + threadIdx.x;
   const bool live = t < T;
-  if (live) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j];
-      if (e >= 0 && e < E) atomicOr(&bits[wave * E + e], 1ull << lane);
-    }
+  // The token's pairs are handled KB at a time: their expert indices, then the expert bases, are
+  // loaded together, so a pair's loads do not wait on the previous pair's stores.
+  constexpr int KB = 8;
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    int e[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) e[i] = (live && j0 + i < k) ? idx[t * k + j0 + i] : -1;
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+      if (e[i] >= 0 && e[i] < E) atomicOr(&bits[wave * E + e[i]], 1ull << lane);
   }
   __syncthreads();
   if (!live) return;
   const unsigned long long below = (1ull << lane) - 1ull;
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[t * k + j];
-    int32_t slot = -1;
-    if (e >= 0 && e < E) {
-      int r = offsets[e] + cc[(int64_t)blockIdx.x * E + e];
-      for (int w = 0; w < wave; ++w) r += __popcll(bits[w * E + e]);
-      r += __popcll(bits[wave * E + e] & below);
-      slot = r;
-      sorted_token[r] = (int32_t)t;
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    int e[KB], base[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      e[i] = j0 + i < k ? idx[t * k + j0 + i] : -1;
+      if (e[i] >= E) e[i] = -1;
     }
-    slot_of_pair[t * k + j] = slot;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) base[i] = e[i] >= 0 ? offsets[e[i]] + cc[(int64_t)blockIdx.x * E + e[i]] : 0;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      if (j0 + i >= k) break;
+      int32_t slot = -1;
+      if (e[i] >= 0) {
+        int r = base[i];
+        for (int w = 0; w < wave; ++w) r += __popcll(bits[w * E + e[i]]);
+        r += __popcll(bits[wave * E + e[i]] & below);
+        slot = r;
+        sorted_token[r] = (int32_t)t;
+      }
+      slot_of_pair[t * k + j0 + i] = slot;
+    }
   }
 }
 

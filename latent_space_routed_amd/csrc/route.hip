@@ -204,80 +204,72 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ sco
 // QB histogram ([tahou] 负载均衡优化: map to 0..1 and bin). A workgroup owns a slice of EB
 // experts for every token: its [EB, NB] counters live in LDS and are added to the caller's
 // histogram with plain read-add-writes (no other workgroup touches those bins), so the result is
-// exact and independent of scheduling. Thread i handles tokens i, i + 512, ...: per token it reads
-// the slice's EB scores (one vector load when the row layout allows), the row's thresholds and
-// its k-th expert index, U tokens at a time so that the loads overlap. Slices are numbered so that
-// the slices on one XCD (workgroup w runs on XCD w % 8) are contiguous experts, and the cache lines
-// of a score row that they share are fetched into that XCD's L2 once.
+// exact and independent of scheduling. Lane l of a wave takes expert e0 + l % EB of token
+// sub-row l / EB, so one load instruction reads 64 / EB tokens' slices as runs of 4 EB contiguous
+// bytes (a run per cache line, where a lane per token would touch a line per lane). The kernel is
+// bound by loads in flight (each workgroup walks all T rows), so every lane issues U = 16 tokens'
+// loads before it uses any, and the slice width leaves at least 192 workgroups. The row's k-th
+// expert index only breaks exact ties with v_k and is loaded only then. Slices are numbered so
+// that the slices on one XCD (workgroup w runs on XCD w % 8) are contiguous experts, and the score
+// lines they share are fetched into that XCD's L2 once.
 // Selection of e by t is decided from the row's k-th value v_k and the k-th expert index e_k (the
 // order is value desc, index asc): e is selected iff s_hat > v_k, or s_hat == v_k and e <= e_k.
 // ------------------------------------------------------------------------------------------------
-constexpr int kHistThreads = 512;
+constexpr int kHistThreads = 1024;
 constexpr int kHistLdsBytes = 128 * 1024;
-constexpr int kHistUnroll = 4;
+constexpr int kHistUnroll = 16;
 
 __device__ inline int xcd_contiguous(int w, int n) {  // bijection on [0, n): XCD x gets a contiguous run
   const int x = w % kXcds, m = w / kXcds, q = n / kXcds, r = n % kXcds;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + m;
 }
 
-template <int EB, bool VEC>
+template <int EB>
 __global__ void __launch_bounds__(kHistThreads)
     qb_hist_kernel(const float* __restrict__ scores, const float* __restrict__ bias, const int32_t* __restrict__ idx,
                    const float* __restrict__ thresh, int T, int E, int k, int nb, uint32_t* __restrict__ hist) {
   extern __shared__ uint32_t cnt[];  // [EB][nb]
+  constexpr int TPW = kWave / EB;                      // tokens per wave per load
+  constexpr int TPB = TPW * (kHistThreads / kWave);    // tokens per workgroup per load
   const int e0 = xcd_contiguous(blockIdx.x, gridDim.x) * EB;
   for (int i = threadIdx.x; i < EB * nb; i += kHistThreads) cnt[i] = 0;
   __syncthreads();
-  float be[EB];
-#pragma unroll
-  for (int j = 0; j < EB; ++j) be[j] = e0 + j < E ? bias[e0 + j] : 0.0f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane % EB;
+  const int e = e0 + j;
+  const bool has_e = e < E;
+  const float be = has_e ? bias[e] : 0.0f;
   const float fnb = (float)nb;
-  for (int tb = 0; tb < T; tb += kHistThreads * kHistUnroll) {
-    float s[kHistUnroll][EB], vk[kHistUnroll], vk1[kHistUnroll];
-    int ek[kHistUnroll];
+  const int t_lane = wave * TPW + lane / EB;
+  for (int tb = 0; tb < T; tb += TPB * kHistUnroll) {
+    float s[kHistUnroll], vk[kHistUnroll], vk1[kHistUnroll];
 #pragma unroll
     for (int u = 0; u < kHistUnroll; ++u) {
-      const int t = tb + u * kHistThreads + threadIdx.x;
-      const bool live = t < T;
-      const int64_t tc = live ? t : 0;
-      const float* row = scores + tc * E + e0;
-      if constexpr (VEC && EB == 4) {
-        const float4 v = *reinterpret_cast<const float4*>(row);
-        s[u][0] = v.x, s[u][1] = v.y, s[u][2] = v.z, s[u][3] = v.w;
-      } else if constexpr (VEC && EB == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(row);
-        s[u][0] = v.x, s[u][1] = v.y;
-      } else {
-#pragma unroll
-        for (int j = 0; j < EB; ++j) s[u][j] = e0 + j < E ? row[j] : 0.0f;
-      }
+      const int t = tb + u * TPB + t_lane;
+      const int64_t tc = t < T ? t : 0;
+      s[u] = has_e ? scores[tc * E + e] : 0.0f;
       vk[u] = thresh[2 * tc];
       vk1[u] = thresh[2 * tc + 1];
-      ek[u] = live ? idx[tc * k + k - 1] : -1;
     }
 #pragma unroll
     for (int u = 0; u < kHistUnroll; ++u) {
-      if (ek[u] < 0) continue;  // past the last token
-#pragma unroll
-      for (int j = 0; j < EB; ++j) {
-        const int e = e0 + j;
-        if (e >= E) continue;
-        const float sh = __fadd_rn(s[u][j], be[j]);
-        const bool sel = sh > vk[u] || (sh == vk[u] && e <= ek[u]);
-        const float m = __fsub_rn(sh, sel ? vk1[u] : vk[u]);
-        float uu = __fmul_rn(__fadd_rn(m, 1.0f), 0.5f);
-        uu = fminf(fmaxf(uu, 0.0f), 1.0f);
-        const int b = min(nb - 1, (int)floorf(__fmul_rn(uu, fnb)));
-        atomicAdd(&cnt[j * nb + b], 1u);
-      }
+      const int t = tb + u * TPB + t_lane;
+      if (!has_e || t >= T) continue;
+      const float sh = __fadd_rn(s[u], be);
+      bool sel = sh > vk[u];
+      if (sh == vk[u]) sel = e <= idx[(int64_t)t * k + k - 1];
+      const float m = __fsub_rn(sh, sel ? vk1[u] : vk[u]);
+      float uu = __fmul_rn(__fadd_rn(m, 1.0f), 0.5f);
+      uu = fminf(fmaxf(uu, 0.0f), 1.0f);
+      const int b = min(nb - 1, (int)floorf(__fmul_rn(uu, fnb)));
+      atomicAdd(&cnt[j * nb + b], 1u);
     }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < EB * nb; i += kHistThreads) {
     const uint32_t c = cnt[i];
-    const int e = e0 + i / nb;
-    if (c != 0 && e < E) hist[(int64_t)e * nb + i % nb] += c;
+    const int ee = e0 + i / nb;
+    if (c != 0 && ee < E) hist[(int64_t)ee * nb + i % nb] += c;
   }
 }
 
@@ -352,35 +344,32 @@ hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int
   return hipGetLastError();
 }
 
-template <int EB, bool VEC>
+template <int EB>
 hipError_t launch_qb_hist_t(const float* scores, const float* bias, const int32_t* idx, const float* thresh, int T,
                             int E, int k, int nb, uint32_t* hist, hipStream_t s) {
   static bool attr_set = false;  // the LDS limit is a property of the function: set once, before any launch
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)qb_hist_kernel<EB, VEC>,
+    const hipError_t e = hipFuncSetAttribute((const void*)qb_hist_kernel<EB>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, kHistLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((qb_hist_kernel<EB, VEC>), dim3((unsigned)ceil_div(E, EB)), dim3(kHistThreads),
-                     (size_t)EB * nb * 4, s, scores, bias, idx, thresh, T, E, k, nb, hist);
+  hipLaunchKernelGGL((qb_hist_kernel<EB>), dim3((unsigned)ceil_div(E, EB)), dim3(kHistThreads), (size_t)EB * nb * 4,
+                     s, scores, bias, idx, thresh, T, E, k, nb, hist);
   return hipGetLastError();
 }
 
 hipError_t launch_qb_hist(const float* scores, const float* bias, const int32_t* idx, const float* thresh, int T,
                           int E, int k, int nb, uint32_t* hist, hipStream_t s) {
   KernelTimer timer("qb_hist", s);
-  // experts per workgroup: the most that still give 256 workgroups (one per CU), within the LDS
-  // budget; vector loads of a slice need E a multiple of EB and an aligned score matrix
-  auto fits = [&](int eb) { return (int64_t)eb * nb * 4 <= kHistLdsBytes; };
-  const int eb = (fits(4) && ceil_div(E, 4) >= 256) ? 4 : (fits(2) && ceil_div(E, 2) >= 256) ? 2 : 1;
-  if (!fits(eb)) return hipErrorInvalidValue;
-  const bool vec = E % eb == 0 && reinterpret_cast<uintptr_t>(scores) % (4 * eb) == 0;
-  if (eb == 4) return vec ? launch_qb_hist_t<4, true>(scores, bias, idx, thresh, T, E, k, nb, hist, s)
-                          : launch_qb_hist_t<4, false>(scores, bias, idx, thresh, T, E, k, nb, hist, s);
-  if (eb == 2) return vec ? launch_qb_hist_t<2, true>(scores, bias, idx, thresh, T, E, k, nb, hist, s)
-                          : launch_qb_hist_t<2, false>(scores, bias, idx, thresh, T, E, k, nb, hist, s);
-  return launch_qb_hist_t<1, false>(scores, bias, idx, thresh, T, E, k, nb, hist, s);
+  // experts per workgroup: the most that still give 192 workgroups, within the LDS budget
+  auto ok = [&](int eb) { return (int64_t)eb * nb * 4 <= kHistLdsBytes && ceil_div(E, eb) >= 192; };
+  const int eb = ok(8) ? 8 : ok(4) ? 4 : ok(2) ? 2 : 1;
+  if ((int64_t)eb * nb * 4 > kHistLdsBytes) return hipErrorInvalidValue;
+  if (eb == 8) return launch_qb_hist_t<8>(scores, bias, idx, thresh, T, E, k, nb, hist, s);
+  if (eb == 4) return launch_qb_hist_t<4>(scores, bias, idx, thresh, T, E, k, nb, hist, s);
+  if (eb == 2) return launch_qb_hist_t<2>(scores, bias, idx, thresh, T, E, k, nb, hist, s);
+  return launch_qb_hist_t<1>(scores, bias, idx, thresh, T, E, k, nb, hist, s);
 }
 
 hipError_t launch_qb_update(uint32_t* hist, int E, int k, int nb, int64_t n_acc, float* bias, hipStream_t s) {
