@@ -301,6 +301,21 @@ def main() -> int:
         layer.forward(x)
         layer.qb_update()
 
+    qb_report = None
+    if cfg.qb_updates > 1:  # the QB loop over distinct batches, the bias carried forward (untimed)
+        from workloads.inputs import token_rows
+
+        log(f"[bench] {cfg.qb_updates} QB updates over batches 0..{cfg.qb_updates - 1}")
+        ratios = []
+        for bt in range(cfg.qb_updates):
+            xb = x if bt == 0 else to_device(token_rows(cfg, 0, bt), cfg.act_dtype)
+            counts = np.diff(layer.forward(xb)["offsets"].cpu().numpy())
+            ratios.append(round(float(counts.max() / counts.mean()), 3))
+            layer.qb_update()
+            del xb
+        qb_report = {"updates": cfg.qb_updates, "max_over_mean_expert_load": ratios,
+                     "note": "load of each batch's forward, before that batch's bias update"}
+
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -365,14 +380,16 @@ def main() -> int:
         "kernels_ms_per_step": kernels,
         "kernels_roofline": kernel_roofline(kernel_work(cfg, offsets, layer.fused), kernels),
     }
+    if qb_report:
+        out["qb"] = qb_report
     if args.backward:
         out["train"] = train_steps(layer, x, cfg, args, _lib, torch)
     if not args.no_mx and cfg.act_dtype == "bf16":
         log("[bench] MX routed experts")
         out["mx"] = mx_steps(cfg, w, x, args, _lib, torch, LatentMoE)
     if not args.no_cpu_baseline:
-        log(f"[bench] timing the CPU oracle on {args.cpu_sample} tokens")
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
+        log(f"[bench] timing the CPU oracle on {min(args.cpu_sample, cfg.T)} tokens")
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_sample, cfg.T))
     print(json.dumps(out), flush=True)
     return 0
 

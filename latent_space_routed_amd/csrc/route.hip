@@ -13,16 +13,37 @@ namespace {
 // wider one). x (bf16) times a bf16 part has a 16-bit significand, so each product is exact in
 // f32 and the router logits accumulate in f32 like an f32 GEMM. Output row e = [hi | mid | lo].
 // ------------------------------------------------------------------------------------------------
+__device__ inline void split3(float v, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  hi = f32_to_bf16(v);
+  const float r1 = v - bf16_to_f32(hi);
+  mid = f32_to_bf16(r1);
+  lo = f32_to_bf16(r1 - bf16_to_f32(mid));
+}
+
+// Eight consecutive weights per thread: two 16-byte loads, one 16-byte store per part (cols a
+// multiple of 8, both matrices 16-byte aligned).
+__global__ void split3_vec_kernel(const float* __restrict__ w, uint16_t* __restrict__ out, int rows, int cols) {
+  const int64_t n8 = (int64_t)rows * cols / 8;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i * 8 / cols, c = i * 8 % cols;
+    const float4 a = reinterpret_cast<const float4*>(w)[2 * i], b = reinterpret_cast<const float4*>(w)[2 * i + 1];
+    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint16_t h[8], m[8], l[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) split3(v[j], h[j], m[j], l[j]);
+    uint16_t* o = out + r * 3 * cols + c;
+    *reinterpret_cast<uint4*>(o) = *reinterpret_cast<const uint4*>(h);
+    *reinterpret_cast<uint4*>(o + cols) = *reinterpret_cast<const uint4*>(m);
+    *reinterpret_cast<uint4*>(o + 2 * (int64_t)cols) = *reinterpret_cast<const uint4*>(l);
+  }
+}
+
 __global__ void split3_kernel(const float* __restrict__ w, uint16_t* __restrict__ out, int rows, int cols) {
   const int64_t n = (int64_t)rows * cols;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t r = i / cols, c = i % cols;
-    const float v = w[i];
-    const uint16_t hi = f32_to_bf16(v);
-    const float r1 = v - bf16_to_f32(hi);
-    const uint16_t mid = f32_to_bf16(r1);
-    const float r2 = r1 - bf16_to_f32(mid);
-    const uint16_t lo = f32_to_bf16(r2);
+    uint16_t hi, mid, lo;
+    split3(w[i], hi, mid, lo);
     uint16_t* o = out + r * 3 * cols + c;
     o[0] = hi;
     o[cols] = mid;
@@ -286,8 +307,20 @@ __global__ void __launch_bounds__(256) qb_update_kernel(uint32_t* __restrict__ h
   uint32_t* h = hist + (int64_t)e * nb;
   const int bpl = (nb + 63) / 64;
   const int j0 = min(nb, lane * bpl), j1 = min(nb, j0 + bpl);
+  // the lane's bins are read once, 16 at a time (all loads in flight together), and kept for the
+  // walk to j*
+  constexpr int R = 16;
+  uint32_t hv[R];
   uint64_t lsum = 0;
-  for (int j = j0; j < j1; ++j) lsum += h[j];
+  const bool cached = j1 - j0 <= R;
+#pragma unroll
+  for (int i = 0; i < R; ++i) hv[i] = (cached && j0 + i < j1) ? h[j0 + i] : 0u;
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) lsum += hv[i];
+  } else {
+    for (int j = j0; j < j1; ++j) lsum += h[j];
+  }
   uint64_t incl = lsum;  // inclusive wave scan
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -299,16 +332,25 @@ __global__ void __launch_bounds__(256) qb_update_kernel(uint32_t* __restrict__ h
     const double c_star = (double)((int64_t)(E - k) * n_acc) / (double)E;
     if ((double)base < c_star && (double)incl >= c_star) {
       uint64_t cum = base;
-      for (int j = j0; j < j1; ++j) {
-        const uint64_t hj = h[j];
+      bool done = false;
+      // bin j holds hj counts: the first bin whose cumulative count reaches c* is j*
+      auto visit = [&](int j, uint64_t hj) __attribute__((always_inline)) {
+        if (done) return;
         if ((double)(cum + hj) >= c_star) {
           const double frac = (c_star - (double)cum) / (double)hj;
           const double u_hat = ((double)j + frac) / (double)nb;
           const double m_hat = 2.0 * u_hat - 1.0;
           bias[e] = (float)((double)bias[e] - m_hat);
-          break;
+          done = true;
         }
         cum += hj;
+      };
+      if (cached) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+          if (j0 + i < j1) visit(j0 + i, hv[i]);
+      } else {
+        for (int j = j0; j < j1 && !done; ++j) visit(j, h[j]);
       }
     }
   }
@@ -326,6 +368,11 @@ void launch_topk_t(const float* s, const float* b, int T, int E, int k, int32_t*
 hipError_t launch_split3(const float* w, uint16_t* out, int rows, int cols, hipStream_t s) {
   KernelTimer timer("router_split", s);
   const int64_t n = (int64_t)rows * cols;
+  if (cols % 8 == 0 && reinterpret_cast<uintptr_t>(w) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) {
+    const unsigned blocks = (unsigned)hmin(ceil_div(n / 8, 256), 8192);
+    hipLaunchKernelGGL(split3_vec_kernel, dim3(blocks), dim3(256), 0, s, w, out, rows, cols);
+    return hipGetLastError();
+  }
   const unsigned blocks = (unsigned)hmin(ceil_div(n, 256), 8192);
   hipLaunchKernelGGL(split3_kernel, dim3(blocks), dim3(256), 0, s, w, out, rows, cols);
   return hipGetLastError();

@@ -76,3 +76,36 @@ def test_route_topk_ordering(name):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(hist.cpu().numpy().view(np.uint32),
                                   O.qb_histogram(s, bias, ref_idx, ref_thr, cfg.n_bins))
+
+
+@pytest.mark.parametrize("nb", [2, 100, 1000, 1024, 1025, 4096, 32768])
+def test_qb_update_bin_counts(nb):
+    """QB bias update on synthetic histograms whose rows each sum to N_acc (concentrated on a band of
+    bins, one row all in one bin, one row spread evenly), bit-exact against the oracle for bin counts
+    that give one to 512 bins per lane (the kernel keeps up to 16 per lane in registers)."""
+    E, k, n_acc = 37, 5, 5000
+    rng = np.random.default_rng(nb)
+    hist = np.zeros((E, nb), dtype=np.uint32)
+    for e in range(E):
+        if e == 0:
+            hist[e, rng.integers(nb)] = n_acc
+        elif e == 1:
+            hist[e] = rng.multinomial(n_acc, np.full(nb, 1.0 / nb))
+        else:
+            c = rng.integers(nb)
+            w = max(1, nb // 20)
+            lo, hi = max(0, c - w), min(nb, c + w + 1)
+            p = np.zeros(nb)
+            p[lo:hi] = 1.0 / (hi - lo)
+            hist[e] = rng.multinomial(n_acc, p)
+    bias0 = (rng.standard_normal(E) * 0.01).astype(np.float32)
+    cfg = replace(CONFIGS["mid_bf16"], T=64, d_model=128, n_experts=E, top_k=k, n_bins=nb)
+    shape = C.make_shape(cfg, 64)
+    hd = torch.from_numpy(hist.view(np.int32).copy()).cuda()
+    bd = torch.from_numpy(bias0.copy()).cuda()
+    say(f"qb_update E={E} k={k} nb={nb} n_acc={n_acc}")
+    C.lmoe_qb_update(shape, hd, n_acc, bd)
+    torch.cuda.synchronize()
+    want, _ = O.qb_update(hist, n_acc, bias0, k)
+    np.testing.assert_array_equal(bd.cpu().numpy(), want)
+    assert not hd.cpu().numpy().any()
