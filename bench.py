@@ -8,8 +8,9 @@ timed region. Prints ONE JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload k3_prefill] [--no-cpu-baseline]
                   [--backward] [--no-mx]
 
-The headline line is the bf16 layer. Under "mx" the same steps are timed with the routed experts on
-MXFP4 weights and MXFP8 activations (a variant with its own numerics, never the headline value).
+The headline line is the bf16 layer, stepped eagerly. Under "graph" the same step is replayed from a
+HIP graph (same kernels, no launch gaps). Under "mx" the same steps are timed with the routed experts
+on MXFP4 weights and MXFP8 activations (a variant with its own numerics, never the headline value).
 """
 from __future__ import annotations
 
@@ -241,6 +242,23 @@ def train_steps(layer, x, cfg, args, _lib, torch) -> dict:
             "backward_kernels_ms_per_step": kernels, "backward_kernels_sum_ms": round(sum(kernels.values()), 4)}
 
 
+def graph_steps(layer, x, cfg, args, torch) -> dict:
+    """The same step (forward + QB update) recorded once as a HIP graph and replayed: the launch
+    gaps between the step's kernels go away; the kernels are the same."""
+    layer.qb_update()  # close the step of the forward that read the offsets
+    g, _ = layer.capture_step(x)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    del g
+    return {"ms_per_step": ms, "tokens_per_s": cfg.T / (ms / 1e3)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,9 +266,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="k3_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=384)
+    ap.add_argument("--cpu-sample", type=int, default=640)
     ap.add_argument("--backward", action="store_true",
                     help="also time training steps (forward + backward + bias update) and report them under 'train'")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the replays of the step recorded as a HIP graph (reported under 'graph')")
     ap.add_argument("--no-mx", action="store_true",
                     help="skip the forward steps with MX routed experts (reported under 'mx')")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -382,6 +402,9 @@ def main() -> int:
     }
     if qb_report:
         out["qb"] = qb_report
+    if not args.no_graph:
+        log("[bench] graph replays")
+        out["graph"] = graph_steps(layer, x, cfg, args, torch)
     if args.backward:
         out["train"] = train_steps(layer, x, cfg, args, _lib, torch)
     if not args.no_mx and cfg.act_dtype == "bf16":

@@ -37,6 +37,8 @@ hipEvent_t take_event() {
 
 KernelTimer::KernelTimer(const char* n, hipStream_t s) : name(n), stream(s), ev0(nullptr) {
   if (!g_enabled) return;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;  // no timing events inside a graph capture
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
   hipEvent_t e = take_event();
   if (e && hipEventRecord(e, s) == hipSuccess) ev0 = e;
 }

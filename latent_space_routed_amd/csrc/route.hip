@@ -2,6 +2,8 @@
 // bias update. All integer results (indices, bins, counts) are exact and order-independent.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace lmoe {
@@ -394,13 +396,15 @@ hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int
 template <int EB>
 hipError_t launch_qb_hist_t(const float* scores, const float* bias, const int32_t* idx, const float* thresh, int T,
                             int E, int k, int nb, uint32_t* hist, hipStream_t s) {
-  static bool attr_set = false;  // the LDS limit is a property of the function: set once, before any launch
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute((const void*)qb_hist_kernel<EB>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kHistLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // the LDS limit is a property of the function: set once per process (thread-safe), before any
+  // launch, so the launch itself is all a graph capture records
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute((const void*)qb_hist_kernel<EB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               kHistLdsBytes);
+  });
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((qb_hist_kernel<EB>), dim3((unsigned)ceil_div(E, EB)), dim3(kHistThreads), (size_t)EB * nb * 4,
                      s, scores, bias, idx, thresh, T, E, k, nb, hist);
   return hipGetLastError();

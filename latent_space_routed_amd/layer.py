@@ -239,6 +239,26 @@ class LatentMoE:
         C.lmoe_qb_update(C.make_shape(self.cfg, 0), self.hist, self.n_acc, self.bias)
         self.n_acc = 0
 
+    def capture_step(self, x: torch.Tensor) -> tuple[torch.cuda.CUDAGraph, dict]:
+        """Record one step, forward(x) then the QB update, as a HIP graph to replay.
+
+        Every call of the step only enqueues kernels (no host synchronisation, no allocation, no
+        memset), so the graph holds the same launches in the same order; a replay recomputes the
+        returned buffers from the current contents of x and moves the bias like an eager step. x
+        and the layer's buffers must stay where they are while the graph is in use. The histogram
+        must be empty at capture (call qb_update first), since each replay updates from one batch.
+        """
+        if self.n_acc != 0:
+            raise RuntimeError("capture_step needs an empty histogram: call qb_update() first")
+        if x.shape[0] > self.max_tokens:
+            self.max_tokens = x.shape[0]
+            self._alloc(x.shape[0])
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            b = self.forward(x)
+            self.qb_update()
+        return g, b
+
 
 def upload_weights(inp: dict, act_dtype: str, device: str = "cuda") -> dict:
     """The seeded host inputs (see workloads.inputs) as device tensors."""
