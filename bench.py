@@ -78,7 +78,7 @@ def kernel_work(cfg, offsets, fused: bool = True) -> dict:
         "router_split": ("hbm", E * D * (4 + 6)),
         "gemm_router": ("mfma", (3 if esz == 2 else 1) * 2.0 * T * D * E),
         "route_topk": ("hbm", T * E * 4 + E * 4 + T * k * 8 + T * 8),
-        "qb_hist": ("hbm", T * E * 4 + E * 4 + T * 8 + T * k * 4 + E * NB * 4 * 2),
+        "qb_hist": ("hbm", T * E * 4 + E * 4 + T * 8 + E * NB * 4 * 2),
         "gemm_down": ("mfma", 2.0 * T * D * L),
         "perm_count": ("hbm", T * k * 4),
         "perm_scan": ("hbm", -(-T // 256) * E * 4 * 2 + (E + 1) * 4),
@@ -266,7 +266,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="k3_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=640)
+    ap.add_argument("--cpu-sample", type=int, default=1024)
     ap.add_argument("--backward", action="store_true",
                     help="also time training steps (forward + backward + bias update) and report them under 'train'")
     ap.add_argument("--no-graph", action="store_true",
