@@ -266,7 +266,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="k3_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1024)
+    ap.add_argument("--cpu-sample", type=int, default=2048)
     ap.add_argument("--backward", action="store_true",
                     help="also time training steps (forward + backward + bias update) and report them under 'train'")
     ap.add_argument("--no-graph", action="store_true",

@@ -324,8 +324,10 @@ __device__ inline void dispatch_na(int na, F&& f) {
 // LDS with the 16-byte chunk c of row k at slot c ^ (k % 16); a B fragment (8 consecutive k of one
 // column) is gathered with 16-bit LDS reads, which the swizzle spreads over distinct banks.
 // NTB: B is streamed through once (the routed experts' W1): its DMA carries the non-temporal hint.
+// XB: B's ring holds XB more stages than A's, and B's K-tiles are issued XB tiles further ahead
+// (two A stages and three B stages of 64-element K-tiles fill the 160 KB of LDS).
 template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, int NS, int KB, Epi EPI, bool BKN = false,
-          bool NTB = false>
+          bool NTB = false, int XB = 0>
 __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_dma_kernel(GemmArgs p_in) {
   GemmArgs p = p_in;
@@ -346,14 +348,18 @@ gemm_dma_kernel(GemmArgs p_in) {
   constexpr int WNO = GLU ? WN / 2 : WN;
   // NS LDS stages of KB bytes of every row per K-tile
   static_assert(NS >= 2 && NS <= 5 && (KB == 64 || KB == 128), "pipeline shape");
+  static_assert(XB == 0 || (XB == 1 && NS == 2), "B runs one K-tile further ahead only on a two-stage A ring");
+  constexpr int NSB = NS + XB;  // stages of B
   constexpr int RPD = 1024 / KB;           // rows per 1 KB DMA block
   constexpr int A_PW = BM / RPD / NW;      // DMA blocks per wave per K-tile
   constexpr int B_PW = BNB / RPD / NW;
   static_assert(A_PW * RPD * NW == BM && B_PW * RPD * NW == BNB, "DMA split");
   static_assert(!GLU || BNO % RPD == 0, "a DMA block stays in one GLU half");
-  constexpr int A_BYTES = BM * KB;
-  constexpr int STAGE = (BM + BNB) * KB;
-  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+  constexpr int A_BYTES = BM * KB;  // one stage of A; the NS stages of A come first, then the NSB of B
+  constexpr int B_BYTES = BNB * KB;
+  constexpr int B_BASE = NS * A_BYTES;
+  constexpr int LDS_BYTES = B_BASE + NSB * B_BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   TileInfo t;
   if (!assign_tile<BM, BNO>(p, t)) return;
@@ -419,28 +425,35 @@ gemm_dma_kernel(GemmArgs p_in) {
       (unsigned)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
 
   int ka = ka0;  // byte offset of the next issued K-tile inside A's (possibly wrapped) row
-  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
-    const unsigned base = lds0 + stage * STAGE;
+  auto issue_a = [&](int kt, int stage) __attribute__((always_inline)) {
+    const unsigned base = lds0 + stage * A_BYTES;
     if (!seg2 || kt < KT1) {
 #pragma unroll
       for (int i = 0; i < A_PW; ++i) dma16(a_desc, a_voff[i], ka, base + (wave * A_PW + i) * 1024);
-#pragma unroll
-      for (int i = 0; i < B_PW; ++i) {
-        const bool up = GLU && (wave * B_PW + i) * RPD >= BNO;
-        const int soff = BKN ? kt * (KB / (int)sizeof(TI)) * (int)b_ld : kt * KB;
-        if constexpr (NTB)
-          dma16_nt(up ? b_desc1 : b_desc0, b_voff[i], soff, base + A_BYTES + (wave * B_PW + i) * 1024);
-        else
-          dma16(up ? b_desc1 : b_desc0, b_voff[i], soff, base + A_BYTES + (wave * B_PW + i) * 1024);
-      }
       ka += KB;
       if (ka == a_wrap) ka = 0;
     } else {
       const int kk = (kt - KT1) * KB;
 #pragma unroll
       for (int i = 0; i < A_PW; ++i) dma16(a2_desc, a2_voff[i], kk, base + (wave * A_PW + i) * 1024);
+    }
+  };
+  auto issue_b = [&](int kt, int stage) __attribute__((always_inline)) {
+    const unsigned base = lds0 + B_BASE + stage * B_BYTES;
+    if (!seg2 || kt < KT1) {
 #pragma unroll
-      for (int i = 0; i < B_PW; ++i) dma16(b2_desc, b2_voff[i], kk, base + A_BYTES + (wave * B_PW + i) * 1024);
+      for (int i = 0; i < B_PW; ++i) {
+        const bool up = GLU && (wave * B_PW + i) * RPD >= BNO;
+        const int soff = BKN ? kt * (KB / (int)sizeof(TI)) * (int)b_ld : kt * KB;
+        if constexpr (NTB)
+          dma16_nt(up ? b_desc1 : b_desc0, b_voff[i], soff, base + (wave * B_PW + i) * 1024);
+        else
+          dma16(up ? b_desc1 : b_desc0, b_voff[i], soff, base + (wave * B_PW + i) * 1024);
+      }
+    } else {
+      const int kk = (kt - KT1) * KB;
+#pragma unroll
+      for (int i = 0; i < B_PW; ++i) dma16(b2_desc, b2_voff[i], kk, base + (wave * B_PW + i) * 1024);
     }
   };
   constexpr int PER_TILE = A_PW + B_PW;  // DMA instructions per wave per K-tile
@@ -462,8 +475,9 @@ gemm_dma_kernel(GemmArgs p_in) {
 
   dispatch_na<WM>(na, [&](auto na_c) __attribute__((always_inline)) {
     constexpr int NA = decltype(na_c)::value;
-    auto compute = [&](int stage) __attribute__((always_inline)) {
-      const char* base = smem + stage * STAGE;
+    auto compute = [&](int sa, int sb) __attribute__((always_inline)) {
+      const char* base = smem + sa * A_BYTES;
+      const char* bbase = smem + B_BASE + sb * B_BYTES;
       // fragments of k-step s + 1 are read from LDS while the MFMAs of k-step s run
       uint4 af[2][NA > 0 ? NA : 1], bf[2][WN];
       auto load = [&](int s, uint4 (&a)[NA > 0 ? NA : 1], uint4 (&b)[WN]) __attribute__((always_inline)) {
@@ -480,11 +494,11 @@ gemm_dma_kernel(GemmArgs p_in) {
             uint16_t v[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-              v[i] = *reinterpret_cast<const uint16_t*>(base + A_BYTES + (k0 + i) * BROW + ((c ^ ((k0 + i) & 15)) << 4) +
+              v[i] = *reinterpret_cast<const uint16_t*>(bbase + (k0 + i) * BROW + ((c ^ ((k0 + i) & 15)) << 4) +
                                                         e * 2);
             b[j] = *reinterpret_cast<const uint4*>(v);
           } else {
-            b[j] = *reinterpret_cast<const uint4*>(base + A_BYTES + bblk * 32 * KB + fo[s]);
+            b[j] = *reinterpret_cast<const uint4*>(bbase + bblk * 32 * KB + fo[s]);
           }
         }
       };
@@ -500,17 +514,39 @@ gemm_dma_kernel(GemmArgs p_in) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    const int pre = min(KT, NS - 1);
-    for (int kt = 0; kt < pre; ++kt) issue(kt, kt);
-    for (int kt = 0; kt < KT; ++kt) {
-      wait_tiles_after(min(KT - kt - 1, NS - 2));  // K-tile kt has landed in LDS (this wave's part)
-      __syncthreads();                             // ... and every wave's; stage kt-1 is free again
-      if (kt + NS - 1 < KT) issue(kt + NS - 1, (kt + NS - 1) % NS);
-      if (NA > 0) compute(kt % NS);
+    if constexpr (XB == 0) {
+      const int pre = min(KT, NS - 1);
+      for (int kt = 0; kt < pre; ++kt) {
+        issue_a(kt, kt);
+        issue_b(kt, kt);
+      }
+      for (int kt = 0; kt < KT; ++kt) {
+        wait_tiles_after(min(KT - kt - 1, NS - 2));  // K-tile kt has landed in LDS (this wave's part)
+        __syncthreads();                             // ... and every wave's; stage kt-1 is free again
+        if (kt + NS - 1 < KT) {
+          issue_a(kt + NS - 1, (kt + NS - 1) % NS);
+          issue_b(kt + NS - 1, (kt + NS - 1) % NS);
+        }
+        if (NA > 0) compute(kt % NS, kt % NS);
+      }
+    } else {
+      // Issue order A0 B0 B1 | A1 B2 | A2 B3 | ...: when A(kt) and B(kt) have landed, only B(kt+1)
+      // can still be in flight (loads complete in issue order).
+      issue_a(0, 0);
+      issue_b(0, 0);
+      if (KT > 1) issue_b(1, 1);
+      for (int kt = 0; kt < KT; ++kt) {
+        if (kt + 1 < KT) wait_vmcnt<B_PW>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // every wave's part has landed; A stage (kt+1)%2 and B stage (kt+2)%3 are free
+        if (kt + 1 < KT) issue_a(kt + 1, (kt + 1) & 1);
+        if (kt + 2 < KT) issue_b(kt + 2, (kt + 2) % 3);
+        if (NA > 0) compute(kt & 1, kt % 3);
+      }
     }
   });
   if constexpr (EPI == Epi::Store || EPI == Epi::Glu) {
-    constexpr int REGION = NS * STAGE / NW;  // each wave's slice of the pipeline LDS
+    constexpr int REGION = LDS_BYTES / NW;  // each wave's slice of the pipeline LDS
     const bool bf = p.c_dtype == LMOE_BF16;
     const int vec = bf ? 8 : 4;
     if (p.N % vec == 0 && p.ldc % vec == 0) {
@@ -1044,9 +1080,17 @@ hipError_t launch_big(const GemmArgs& a, Epi epi, hipStream_t s) {
                          a);
     return hipGetLastError();
   }
+  // The routed experts' GEMMs stream their weights (B) from HBM once: B runs a three-stage ring
+  // one K-tile further ahead than A (measured at K3 prefill: GEMM1 1.43 -> 1.29 ms, GEMM2 0.92 ->
+  // 0.90 ms; the dense GEMMs, whose B comes from L2, lose 2-5 % with it and keep two stages).
   if (epi == Epi::Glu && a.goff) {  // routed GEMM1: W1 slices streamed with the non-temporal hint
-    hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Glu, false, true>), grid, block, 0,
-                       s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Glu, false, true, 1>), grid,
+                       block, 0, s, a);
+    return hipGetLastError();
+  }
+  if (epi == Epi::Store && a.goff && !a.koff && !a.A2 && a.splits <= 1) {  // routed GEMM2
+    hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Store, false, false, 1>), grid,
+                       block, 0, s, a);
     return hipGetLastError();
   }
   LMOE_LAUNCH_EPI(gemm_dma_kernel, TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes)
