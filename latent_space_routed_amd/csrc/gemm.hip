@@ -1082,9 +1082,15 @@ hipError_t launch_big(const GemmArgs& a, Epi epi, hipStream_t s) {
   }
   // The routed experts' GEMMs stream their weights (B) from HBM once: B runs a three-stage ring
   // one K-tile further ahead than A (measured at K3 prefill: GEMM1 1.43 -> 1.29 ms, GEMM2 0.92 ->
-  // 0.90 ms; the dense GEMMs, whose B comes from L2, lose 2-5 % with it and keep two stages).
+  // 0.90 ms; the backward's recomputed GEMM1 2.69 -> 2.58 ms; the dense GEMMs, whose B comes from
+  // L2, the router's split-K halves and the [K, N]-B products lose 1-5 % with it and keep two stages).
   if (epi == Epi::Glu && a.goff) {  // routed GEMM1: W1 slices streamed with the non-temporal hint
     hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Glu, false, true, 1>), grid,
+                       block, 0, s, a);
+    return hipGetLastError();
+  }
+  if (epi == Epi::GluBwd && a.goff && !a.koff) {  // backward: routed GEMM1 recomputed, W1 streamed
+    hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::GluBwd, false, false, 1>), grid,
                        block, 0, s, a);
     return hipGetLastError();
   }
