@@ -328,8 +328,9 @@ __device__ inline void dispatch_na(int na, F&& f) {
 // (two A stages and three B stages of 64-element K-tiles fill the 160 KB of LDS).
 template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, int NS, int KB, Epi EPI, bool BKN = false,
           bool NTB = false, int XB = 0>
-__global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
-gemm_dma_kernel(GemmArgs p_in) {
+__global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
+    __attribute__((amdgpu_waves_per_eu(WAVES_M* WAVES_N / 4, WAVES_M* WAVES_N / 4)))  // one workgroup per CU
+    gemm_dma_kernel(GemmArgs p_in) {
   GemmArgs p = p_in;
   int ka0 = 0;  // byte offset inside A's wrapped row where this workgroup's K range starts
   if (p.splits > 1) {  // split-K (one K segment, no groups): K-chunk blockIdx.y into its own f32 partial
