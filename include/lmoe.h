@@ -299,8 +299,11 @@ lmoe_status lmoe_grouped_situ_glu_mx(const lmoe_shape* shape, int32_t n_groups, 
 /* Kernel timing for measurement. When enabled, every kernel the library enqueues is bracketed by
  * HIP events on its stream. lmoe_profile_collect() synchronises those events and folds them into
  * per-kernel totals; lmoe_profile_get() reads the totals of kernel `name` (count of launches and
- * summed milliseconds). Host-side state, not thread-safe: a measurement aid only. */
+ * summed milliseconds). lmoe_profile_only(name) restricts the timing to the kernels named `name`
+ * (NULL: every kernel again), so that a timed region carries only the events it needs; `name` is
+ * copied. Host-side state, not thread-safe: a measurement aid only. */
 void lmoe_profile_enable(int on);
+void lmoe_profile_only(const char* name);
 void lmoe_profile_reset(void);
 lmoe_status lmoe_profile_collect(void);
 int lmoe_profile_get(const char* name, int64_t* launches, double* total_ms);

@@ -26,7 +26,8 @@ EXPORTS = ("lmoe_workspace_bytes", "lmoe_status_string", "lmoe_route", "lmoe_qb_
            "lmoe_permute", "lmoe_grouped_situ_glu", "lmoe_pack_shared", "lmoe_combine_norm_up",
            "lmoe_bwd_transpose_weights", "lmoe_bwd_up", "lmoe_bwd_combine_norm", "lmoe_bwd_router",
            "lmoe_bwd_experts", "lmoe_bwd_down", "lmoe_bwd_shared", "lmoe_mx_quantize", "lmoe_grouped_situ_glu_mx",
-           "lmoe_profile_enable", "lmoe_profile_reset", "lmoe_profile_collect", "lmoe_profile_get")
+           "lmoe_profile_enable", "lmoe_profile_only", "lmoe_profile_reset", "lmoe_profile_collect",
+           "lmoe_profile_get")
 
 
 class LmoeError(RuntimeError):
@@ -86,6 +87,7 @@ def lib() -> ctypes.CDLL:
                                                          ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_int32, _P,
                                                          _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "lmoe_profile_enable": (None, [ctypes.c_int]),
+            "lmoe_profile_only": (None, [ctypes.c_char_p]),
             "lmoe_profile_reset": (None, []),
             "lmoe_profile_collect": (ctypes.c_int, []),
             "lmoe_profile_get": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
@@ -247,6 +249,11 @@ def lmoe_grouped_situ_glu_mx(shape, G, rows, K, inter, n_out, a_codes, a_scales,
 
 def profile_enable(on: bool) -> None:
     lib().lmoe_profile_enable(1 if on else 0)
+
+
+def profile_only(name: str | None) -> None:
+    """Time only the kernels named ``name`` (None: every kernel)."""
+    lib().lmoe_profile_only(name.encode() if name else None)
 
 
 def profile_reset() -> None:

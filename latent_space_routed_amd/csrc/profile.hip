@@ -18,6 +18,7 @@ struct Total {
 };
 
 bool g_enabled = false;
+std::string g_only;  // when not empty, the one kernel name that is timed
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_pool;
 std::map<std::string, Total> g_totals;
@@ -37,6 +38,7 @@ hipEvent_t take_event() {
 
 KernelTimer::KernelTimer(const char* n, hipStream_t s) : name(n), stream(s), ev0(nullptr) {
   if (!g_enabled) return;
+  if (!g_only.empty() && (n == nullptr || g_only != n)) return;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;  // no timing events inside a graph capture
   if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
   hipEvent_t e = take_event();
@@ -59,6 +61,8 @@ KernelTimer::~KernelTimer() {
 extern "C" {
 
 void lmoe_profile_enable(int on) { lmoe::g_enabled = on != 0; }
+
+void lmoe_profile_only(const char* name) { lmoe::g_only = name ? name : ""; }
 
 void lmoe_profile_reset(void) { lmoe::g_totals.clear(); }
 
