@@ -109,3 +109,43 @@ def test_qb_update_bin_counts(nb):
     want, _ = O.qb_update(hist, n_acc, bias0, k)
     np.testing.assert_array_equal(bd.cpu().numpy(), want)
     assert not hd.cpu().numpy().any()
+
+
+def test_topk_candidate_pass_boundary():
+    """Rows built through an identity router (the logit of expert e is x[t, e]) so that the number of
+    keys at or above the (k+1)-th largest lane maximum is exactly 64 (the candidate pass's limit,
+    all tied), 65 (one more tie: the exact pass), 128 (every expert tied), 63 tied plus one more in
+    a lane that already holds a tied expert, and distinct values. Selection must follow value
+    descending, index ascending in every case."""
+    T, D, E, k = 5, 128, 128, 8
+    cfg = replace(CONFIGS["mid_bf16"], T=T, d_model=D, n_experts=E, top_k=k, n_bins=1000)
+    x = np.full((T, D), -1.0, dtype=np.float32)
+    x[0, :64] = 2.0                                   # lanes 0..63 each hold one tied key: 64 candidates
+    x[1, :64] = 2.0
+    x[1, 64] = 2.0                                    # lane 0's second expert ties too: 65 candidates
+    x[2, :] = 0.0                                     # all 128 experts tied
+    x[3, :63] = 2.0
+    x[3, 100] = 2.0                                   # lane 36 holds experts 36 and 100, both tied
+    x[4, :] = np.random.default_rng(5).standard_normal(D).astype(np.float32)  # distinct values
+    x = O.store(x, "bf16").astype(np.float32)
+    w_router = np.eye(E, D, dtype=np.float32)
+    bias = np.zeros(E, dtype=np.float32)
+    dev = "cuda"
+    shape = C.make_shape(cfg, T)
+    scores = torch.empty(T, E, dtype=torch.float32, device=dev)
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    wts = torch.empty(T, k, dtype=torch.float32, device=dev)
+    thr = torch.empty(T, 2, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(C.workspace_bytes(shape, C.LMOE_CALL_ROUTE), 256), dtype=torch.uint8, device=dev)
+    say("route: candidate-pass boundary rows (64, 65, 128 tied candidates)")
+    C.lmoe_route(shape, torch.as_tensor(x).to(torch.bfloat16).to(dev), torch.as_tensor(w_router).to(dev),
+                 torch.as_tensor(bias).to(dev), None, scores, idx, wts, thr, ws)
+    torch.cuda.synchronize()
+    s = scores.cpu().numpy()
+    ref_idx, ref_w, ref_thr = O.select_topk(s, bias, k)
+    assert (s[0, :64] == s[0, 0]).all() and (s[2] == s[2, 0]).all()  # the ties are exact
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_array_equal(ref_idx[0], np.arange(k))
+    np.testing.assert_array_equal(ref_idx[2], np.arange(k))
+    np.testing.assert_array_equal(thr.cpu().numpy(), ref_thr)
+    np.testing.assert_allclose(wts.cpu().numpy(), ref_w, rtol=3e-7, atol=0)
