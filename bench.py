@@ -61,6 +61,22 @@ def glu_bytes(cfg, offsets) -> tuple[float, float]:
     return float(w_bytes + a_bytes + h_bytes), flops
 
 
+def router_fused_splits(cfg) -> int:
+    """Number of split-K halves whose partial logits the top-k kernel sums itself (0: the router GEMM
+    stores the scores): the library's rule for bf16 router GEMMs whose 256x256 tiles fill between a
+    quarter and all of the CUs."""
+    if cfg.act_dtype != "bf16":
+        return 0
+    tiles = -(-cfg.T // 256) * -(-cfg.n_experts // 256)
+    if not 64 <= tiles < 256:
+        return 0
+    K = 3 * cfg.d_model
+    for n in range(-(-256 // tiles), 5):
+        if K % n == 0 and (K // n) % 64 == 0 and K // n >= 256:
+            return n
+    return 0
+
+
 def kernel_work(cfg, offsets, fused: bool = True) -> dict:
     """Algorithmic work of each kernel for one forward: ("mfma", FLOPs) for the contractions,
     ("hbm", bytes) for the rest. GEMM FLOPs count only real rows; routed weights count only the
@@ -77,7 +93,9 @@ def kernel_work(cfg, offsets, fused: bool = True) -> dict:
     work = {
         "router_split": ("hbm", E * D * (4 + 6)),
         "gemm_router": ("mfma", (3 if esz == 2 else 1) * 2.0 * T * D * E),
-        "route_topk": ("hbm", T * E * 4 + E * 4 + T * k * 8 + T * 8),
+        # fused: n partial logit matrices read and the scores written; else the scores read
+        "route_topk": ("hbm", (router_fused_splits(cfg) + 1 if router_fused_splits(cfg) else 1) * T * E * 4
+                       + E * 4 + T * k * 8 + T * 8),
         "qb_hist": ("hbm", T * E * 4 + E * 4 + T * 8 + E * NB * 4 * 2),
         "gemm_down": ("mfma", 2.0 * T * D * L),
         "perm_count": ("hbm", T * k * 4),

@@ -173,6 +173,12 @@ lmoe_status lmoe_route(const lmoe_shape* sh, const void* x, const float* w_route
   }
   const SplitPlan sp = router_plan(sh);
   float* part = split_region(sp, T, E, workspace, workspace_bytes, need);
+  if (part && sp.big) {  // a few halves of K on the DMA pipeline: the top-k sums them itself
+    st = hip_status(launch_gemm_split(a, sh->act_dtype, Epi::Sigmoid, sp, part, s, false));
+    if (st != LMOE_OK) return st;
+    return hip_status(launch_topk_partials(part, sp.splits, logit_offset, scores, bias, T, E, sh->top_k, topk_idx,
+                                           topk_w, thresh, s));
+  }
   st = hip_status(run_gemm(a, sh->act_dtype, Epi::Sigmoid, dense_shape(T, ceil_div(E, 256)), sp, part, s));
   if (st != LMOE_OK) return st;
   return hip_status(launch_topk(scores, bias, T, E, sh->top_k, topk_idx, topk_w, thresh, s));

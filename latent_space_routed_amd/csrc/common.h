@@ -164,9 +164,10 @@ SplitPlan plan_split_k(int64_t M, int64_t n_cols, int K1, int K2, int a_kwrap, i
 SplitPlan plan_split_k_big(int64_t M, int64_t n_cols, int K1, int K2, int esz);
 size_t split_k_bytes(const SplitPlan& sp, int64_t M, int64_t n_cols);
 // Runs a (dense, non-gathered) GEMM as the planned split plus the reducing epilogue; partials holds
-// split_k_bytes() bytes.
+// split_k_bytes() bytes, split s of output row m at partials + (s * M + m) * n_cols. With reduce =
+// false only the partial products are written (the caller's next kernel sums them).
 hipError_t launch_gemm_split(const GemmArgs& a, int in_dtype, Epi epi, const SplitPlan& sp, float* partials,
-                             hipStream_t s);
+                             hipStream_t s, bool reduce = true);
 
 enum class GemmShape : int { Big = 0, Small = 1 };
 
@@ -205,6 +206,11 @@ hipError_t launch_unpermute(const void* src, const int32_t* slot_of_pair, int T,
 hipError_t launch_split3(const float* w, uint16_t* out, int rows, int cols, hipStream_t s);
 hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* idx, float* w,
                        float* thresh, hipStream_t s);
+// The router's split-K reduction fused with the top-k: scores = sigmoid(sum of the `splits` partial
+// logits in split order + logit_offset), written to `scores` and selected from registers.
+hipError_t launch_topk_partials(const float* partials, int splits, const float* logit_offset, float* scores,
+                                const float* bias, int T, int E, int k, int32_t* idx, float* w, float* thresh,
+                                hipStream_t s);
 hipError_t launch_qb_hist(const float* scores, const float* bias, const int32_t* idx, const float* thresh, int T,
                           int E, int k, int nb, uint32_t* hist, hipStream_t s);
 hipError_t launch_qb_update(uint32_t* hist, int E, int k, int nb, int64_t n_acc, float* bias, hipStream_t s);

@@ -1191,7 +1191,7 @@ size_t split_k_bytes(const SplitPlan& sp, int64_t M, int64_t n_cols) {
 }
 
 hipError_t launch_gemm_split(const GemmArgs& a, int in_dtype, Epi epi, const SplitPlan& sp, float* partials,
-                             hipStream_t s) {
+                             hipStream_t s, bool reduce) {
   const bool glu = epi == Epi::Glu;
   const int n_cols = glu ? 2 * a.N : a.N;
   if (sp.splits < 2 || a.goff || a.koff || a.a_rows || epi == Epi::GluBwd || (glu && a.glu_up_off != a.N))
@@ -1229,6 +1229,7 @@ hipError_t launch_gemm_split(const GemmArgs& a, int in_dtype, Epi epi, const Spl
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (!reduce) return hipSuccess;
   KernelTimer timer("splitk_reduce", s);
   const int64_t quads = (int64_t)a.M * a.N / 4;
   const dim3 grid((unsigned)ceil_div(quads, 256));

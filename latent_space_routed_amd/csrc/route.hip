@@ -72,6 +72,10 @@ __global__ void split3_kernel(const float* __restrict__ w, uint16_t* __restrict_
 //
 // Either way the winners meet in LDS so that lane r holds the r-th, and the routing weights are
 // normalised by a fixed-order tree over lanes 0..k-1.
+//
+// PART: the scores are first made from the router GEMM's split-K partial logits (summed in split
+// order, plus the logit offset, then the sigmoid: the reduction's own arithmetic), stored, and
+// selected from the same registers.
 // ------------------------------------------------------------------------------------------------
 __device__ inline uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
@@ -82,26 +86,42 @@ __device__ inline float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-template <int NPL>
-__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ scores, const float* __restrict__ bias,
+template <int NPL, bool PART>
+__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ scores, const float* __restrict__ part,
+                                                   int splits, const float* __restrict__ offset,
+                                                   float* __restrict__ scores_out, const float* __restrict__ bias,
                                                    int T, int E, int k, int32_t* __restrict__ idx,
                                                    float* __restrict__ w, float* __restrict__ thresh) {
   __shared__ int win_e[4][65];  // ranks 0..k, k <= 64
   __shared__ uint32_t win_key[4][65];
+  __shared__ float win_s[4][65];
   __shared__ int cand_e[4][64];
   __shared__ uint32_t cand_key[4][64];
+  __shared__ float cand_s[4][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 4 + wv;
   if (t >= T) return;  // the whole wave leaves together
-  const float* row = scores + t * E;
   uint32_t key[NPL];
+  float sv[NPL];  // the unbiased scores, for the routing weights
   uint32_t present = 0;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
     key[i] = 0;
+    sv[i] = 0.0f;
     if (e < E) {
-      key[i] = order_key(row[e] + bias[e]);
+      float sc;
+      if constexpr (PART) {
+        float v = 0.0f;
+        for (int sp = 0; sp < splits; ++sp) v += part[((int64_t)sp * T + t) * E + e];
+        const float x = v + (offset ? offset[e] : 0.0f);
+        sc = 1.0f / (1.0f + expf(-x));
+        scores_out[t * E + e] = sc;
+      } else {
+        sc = scores[t * E + e];
+      }
+      sv[i] = sc;
+      key[i] = order_key(sc + bias[e]);
       present |= 1u << i;
     }
   }
@@ -147,12 +167,14 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ sco
       if (((present >> i) & 1u) && key[i] >= t0) {
         cand_key[wv][pos] = key[i];
         cand_e[wv][pos] = lane + 64 * i;
+        cand_s[wv][pos] = sv[i];
         ++pos;
       }
     __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in issue order
     const bool have = lane < n_cand;
     const uint32_t ck = have ? cand_key[wv][lane] : 0u;
     const int ce = have ? cand_e[wv][lane] : 0;
+    const float cs = have ? cand_s[wv][lane] : 0.0f;
     int place = 0;
     for (int j = 0; j < n_cand; ++j) {
       const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)ck, j);
@@ -162,6 +184,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ sco
     if (have && place < kk) {
       win_e[wv][place] = ce;
       win_key[wv][place] = ck;
+      win_s[wv][place] = cs;
     }
   } else {
     // exact pass
@@ -205,11 +228,12 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ sco
       if ((sel >> i) & 1u) {
         win_e[wv][place[i]] = lane + 64 * i;
         win_key[wv][place[i]] = key[i];
+        win_s[wv][place[i]] = sv[i];
       }
   }
   __builtin_amdgcn_wave_barrier();
   const int my_idx = lane < k ? win_e[wv][lane] : 0;
-  const float my_s = lane < k ? row[my_idx] : 0.0f;
+  const float my_s = lane < k ? win_s[wv][lane] : 0.0f;
   float sum = my_s;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d);
@@ -359,10 +383,24 @@ __global__ void __launch_bounds__(256) qb_update_kernel(uint32_t* __restrict__ h
   for (int j = j0; j < j1; ++j) h[j] = 0;
 }
 
-template <int NPL>
-void launch_topk_t(const float* s, const float* b, int T, int E, int k, int32_t* idx, float* w, float* th,
-                   hipStream_t st) {
-  hipLaunchKernelGGL(topk_kernel<NPL>, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0, st, s, b, T, E, k, idx, w, th);
+template <int NPL, bool PART>
+void launch_topk_t(const float* s, const float* part, int splits, const float* off, float* s_out, const float* b, int T,
+                   int E, int k, int32_t* idx, float* w, float* th, hipStream_t st) {
+  hipLaunchKernelGGL((topk_kernel<NPL, PART>), dim3((unsigned)ceil_div(T, 4)), dim3(256), 0, st, s, part, splits, off,
+                     s_out, b, T, E, k, idx, w, th);
+}
+
+template <bool PART>
+hipError_t launch_topk_any(const float* s, const float* part, int splits, const float* off, float* s_out,
+                           const float* b, int T, int E, int k, int32_t* idx, float* w, float* th, hipStream_t st) {
+  const int npl = (int)ceil_div(E, 64);
+  if (npl <= 2) launch_topk_t<2, PART>(s, part, splits, off, s_out, b, T, E, k, idx, w, th, st);
+  else if (npl <= 4) launch_topk_t<4, PART>(s, part, splits, off, s_out, b, T, E, k, idx, w, th, st);
+  else if (npl <= 8) launch_topk_t<8, PART>(s, part, splits, off, s_out, b, T, E, k, idx, w, th, st);
+  else if (npl <= 16) launch_topk_t<16, PART>(s, part, splits, off, s_out, b, T, E, k, idx, w, th, st);
+  else if (npl <= 32) launch_topk_t<32, PART>(s, part, splits, off, s_out, b, T, E, k, idx, w, th, st);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -383,14 +421,14 @@ hipError_t launch_split3(const float* w, uint16_t* out, int rows, int cols, hipS
 hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* idx, float* w,
                        float* thresh, hipStream_t s) {
   KernelTimer timer("route_topk", s);
-  const int npl = (int)ceil_div(E, 64);
-  if (npl <= 2) launch_topk_t<2>(scores, bias, T, E, k, idx, w, thresh, s);
-  else if (npl <= 4) launch_topk_t<4>(scores, bias, T, E, k, idx, w, thresh, s);
-  else if (npl <= 8) launch_topk_t<8>(scores, bias, T, E, k, idx, w, thresh, s);
-  else if (npl <= 16) launch_topk_t<16>(scores, bias, T, E, k, idx, w, thresh, s);
-  else if (npl <= 32) launch_topk_t<32>(scores, bias, T, E, k, idx, w, thresh, s);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  return launch_topk_any<false>(scores, nullptr, 0, nullptr, nullptr, bias, T, E, k, idx, w, thresh, s);
+}
+
+hipError_t launch_topk_partials(const float* partials, int splits, const float* logit_offset, float* scores,
+                                const float* bias, int T, int E, int k, int32_t* idx, float* w, float* thresh,
+                                hipStream_t s) {
+  KernelTimer timer("route_topk", s);
+  return launch_topk_any<true>(nullptr, partials, splits, logit_offset, scores, bias, T, E, k, idx, w, thresh, s);
 }
 
 template <int EB>
