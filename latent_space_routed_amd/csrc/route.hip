@@ -104,17 +104,26 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ sco
   uint32_t key[NPL];
   float sv[NPL];  // the unbiased scores, for the routing weights
   uint32_t present = 0;
+  if constexpr (PART) {  // split by split, all of the lane's loads of one split in flight together
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) sv[i] = 0.0f;
+    for (int sp = 0; sp < splits; ++sp) {
+      const float* prow = part + ((int64_t)sp * T + t) * E;
+      float pv[NPL];
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) pv[i] = lane + 64 * i < E ? prow[lane + 64 * i] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) sv[i] += pv[i];
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int e = lane + 64 * i;
     key[i] = 0;
-    sv[i] = 0.0f;
     if (e < E) {
       float sc;
       if constexpr (PART) {
-        float v = 0.0f;
-        for (int sp = 0; sp < splits; ++sp) v += part[((int64_t)sp * T + t) * E + e];
-        const float x = v + (offset ? offset[e] : 0.0f);
+        const float x = sv[i] + (offset ? offset[e] : 0.0f);
         sc = 1.0f / (1.0f + expf(-x));
         scores_out[t * E + e] = sc;
       } else {
@@ -123,6 +132,8 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ sco
       sv[i] = sc;
       key[i] = order_key(sc + bias[e]);
       present |= 1u << i;
+    } else {
+      sv[i] = 0.0f;
     }
   }
   const int kk = k + 1;
