@@ -19,7 +19,7 @@ from .gpu_helpers import cached_inputs, device_layer, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,mx", [("mid_bf16", False), ("k3_decode", False), ("mid_bf16", True)])
+@pytest.mark.parametrize("name,mx", [("mid_bf16", False), ("k3_decode", False), ("k3_prefill", False), ("mid_bf16", True)])
 def test_graph_replays_match_eager(name, mx):
     cfg = CONFIGS[name]
     inp = cached_inputs(cfg)
