@@ -104,10 +104,10 @@ __device__ inline void dma16(const u32x4& desc, int voff, int soff, unsigned lds
 }
 
 // The same with the non-temporal hint: for operands streamed through once (the routed experts' W1
-// slices), so that they do not displace the gathered latent rows that the other n-tiles of the
-// same expert read again (measured: routed GEMM1 1.54 -> 1.42 ms at K3 prefill; GEMM2, the dense
-// GEMMs and the MX pipeline gain nothing or lose). A template instance of its own, so that the
-// other GEMMs keep their code.
+// and W2 slices), so that they do not displace the rows that the other n-tiles of the same expert
+// read again (measured at K3 prefill: routed GEMM1 1.54 -> 1.42 ms; GEMM2, on the three-stage B
+// ring, 0.92 -> 0.91 ms; the dense GEMMs and the MX pipeline gain nothing or lose). A template
+// instance of its own, so that the other GEMMs keep their code.
 __device__ inline void dma16_nt(const u32x4& desc, int voff, int soff, unsigned lds_addr) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
                :
@@ -1095,8 +1095,8 @@ hipError_t launch_big(const GemmArgs& a, Epi epi, hipStream_t s) {
                        block, 0, s, a);
     return hipGetLastError();
   }
-  if (epi == Epi::Store && a.goff && !a.koff && !a.A2 && a.splits <= 1) {  // routed GEMM2
-    hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Store, false, false, 1>), grid,
+  if (epi == Epi::Store && a.goff && !a.koff && !a.A2 && a.splits <= 1) {  // routed GEMM2: W2 streamed, non-temporal
+    hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Store, false, true, 1>), grid,
                        block, 0, s, a);
     return hipGetLastError();
   }
