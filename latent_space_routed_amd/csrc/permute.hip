@@ -8,10 +8,14 @@
 //             waves) + popcount(mask_e & lanes below t). Tokens therefore ascend inside an expert.
 //   gather  : one wave per token loads its latent row once and writes it to its k sorted rows.
 // An expert index outside [0, E) drops the pair: its slot is -1 and later kernels skip it.
+#include <mutex>
+
 #include "common.h"
 
 namespace lmoe {
 namespace {
+
+constexpr int kMaxExpertsLds = 2048;  // the library's largest expert count
 
 __global__ void __launch_bounds__(kPermChunk) perm_count_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
                                                                  int32_t* __restrict__ cc) {
@@ -79,9 +83,12 @@ __global__ void __launch_bounds__(kPermChunk) perm_scatter_kernel(const int32_t*
                                                                    const int32_t* __restrict__ offsets,
                                                                    int32_t* __restrict__ sorted_token,
                                                                    int32_t* __restrict__ slot_of_pair) {
-  extern __shared__ unsigned long long bits[];  // [4][E]
+  extern __shared__ unsigned long long bits[];  // [4][E] masks, then [E] i32 bases of this chunk
   constexpr int W = kPermChunk / 64;
+  int32_t* base_e = reinterpret_cast<int32_t*>(bits + W * E);
   for (int i = threadIdx.x; i < W * E; i += kPermChunk) bits[i] = 0ull;
+  // the chunk's first slot in every expert, read once with coalesced loads
+  for (int e = threadIdx.x; e < E; e += kPermChunk) base_e[e] = offsets[e] + cc[(int64_t)blockIdx.x * E + e];
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * kPermChunk + threadIdx.x;
@@ -108,7 +115,7 @@ __global__ void __launch_bounds__(kPermChunk) perm_scatter_kernel(const int32_t*
       if (e[i] >= E) e[i] = -1;
     }
 #pragma unroll
-    for (int i = 0; i < KB; ++i) base[i] = e[i] >= 0 ? offsets[e[i]] + cc[(int64_t)blockIdx.x * E + e[i]] : 0;
+    for (int i = 0; i < KB; ++i) base[i] = e[i] >= 0 ? base_e[e[i]] : 0;
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
       if (j0 + i >= k) break;
@@ -191,8 +198,16 @@ hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* offs
   }
   {
     KernelTimer timer("perm_scatter", s);
-    hipLaunchKernelGGL(perm_scatter_kernel, dim3(chunks), dim3(kPermChunk), (size_t)E * 8 * (kPermChunk / 64), s, idx,
-                       T, E, k, cc, offsets, sorted_token, slot_of_pair);
+    // the masks and bases pass the default 64 KB of dynamic LDS at the largest expert counts
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+      attr = hipFuncSetAttribute((const void*)perm_scatter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 kMaxExpertsLds * (8 * (kPermChunk / 64) + 4));
+    });
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(chunks), dim3(kPermChunk), (size_t)E * (8 * (kPermChunk / 64) + 4), s,
+                       idx, T, E, k, cc, offsets, sorted_token, slot_of_pair);
   }
   return hipGetLastError();
 }

@@ -149,3 +149,32 @@ def test_topk_candidate_pass_boundary():
     np.testing.assert_array_equal(ref_idx[2], np.arange(k))
     np.testing.assert_array_equal(thr.cpu().numpy(), ref_thr)
     np.testing.assert_allclose(wts.cpu().numpy(), ref_w, rtol=3e-7, atol=0)
+
+
+@pytest.mark.parametrize("E", [2048, 1001])
+def test_permute_large_expert_counts(E):
+    """The permutation at expert counts whose per-chunk masks and bases need more than the default
+    64 KB of LDS (E = 2048, the largest the library takes) and at an odd count, on random routing
+    with some experts left empty: offsets, sorted tokens and slots bit-exact against the oracle."""
+    T, D, k = 700, 128, 16
+    cfg = replace(CONFIGS["mid_bf16"], T=T, d_model=D, n_experts=E, top_k=k)
+    rng = np.random.default_rng(E)
+    # each token picks k distinct experts from the first 3/4 of the experts: the rest stay empty
+    idx = np.stack([rng.choice(3 * E // 4, k, replace=False) for _ in range(T)]).astype(np.int32)
+    dev = "cuda"
+    L = cfg.d_latent
+    shape = C.make_shape(cfg, T)
+    x = torch.randn(T, D, device=dev).to(torch.bfloat16)
+    w_down = (torch.randn(L, D, device=dev) * D ** -0.5).to(torch.bfloat16)
+    x_lat = torch.empty(T, L, dtype=torch.bfloat16, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    st = torch.empty(T * k, dtype=torch.int32, device=dev)
+    sp = torch.empty(T * k, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(C.workspace_bytes(shape, C.LMOE_CALL_PERMUTE), 256), dtype=torch.uint8, device=dev)
+    say(f"permute: T={T} E={E} k={k}")
+    C.lmoe_permute(shape, x, w_down, torch.as_tensor(idx).to(dev), x_lat, off, st, sp, None, ws)
+    torch.cuda.synchronize()
+    ref_off, ref_st, ref_sp = O.permute(idx, E)
+    np.testing.assert_array_equal(off.cpu().numpy(), ref_off)
+    np.testing.assert_array_equal(st.cpu().numpy(), ref_st)
+    np.testing.assert_array_equal(sp.cpu().numpy(), ref_sp)
