@@ -6,11 +6,17 @@ combine + RMSNorm + up-projection, and the QB bias update. Inputs are resident i
 timed region. Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload k3_prefill] [--no-cpu-baseline]
-                  [--backward] [--no-mx]
+                  [--backward] [--no-mx] [--no-graph] [--no-configs]
 
-The headline line is the bf16 layer, stepped eagerly. Under "graph" the same step is replayed from a
-HIP graph (same kernels, no launch gaps). Under "mx" the same steps are timed with the routed experts
-on MXFP4 weights and MXFP8 activations (a variant with its own numerics, never the headline value).
+Timing: two pre-generated batches alternate step by step (so the timed routing is not the one the
+bias was fitted to in warm-up; the bias update runs every step); before each timed step a 512 MB
+buffer is written to flush the 256 MB MALL (outside the timed region); every step is bracketed by
+HIP events on the launch stream, and ms_per_step is the median (min and mean reported beside it).
+The headline line is the bf16 layer at k3_prefill, stepped eagerly. Under "configs" the other
+workloads (tiny, mid, K3 decode, K3 stress) are timed the same way. Under "graph" the same step is
+replayed from a HIP graph (same kernels, no launch gaps). Under "mx" the same steps are timed with
+the routed experts on MXFP4 weights and MXFP8 activations (a variant with its own numerics, never
+the headline value).
 """
 from __future__ import annotations
 
@@ -93,9 +99,9 @@ def kernel_work(cfg, offsets, fused: bool = True) -> dict:
     work = {
         "router_split": ("hbm", E * D * (4 + 6)),
         "gemm_router": ("mfma", (3 if esz == 2 else 1) * 2.0 * T * D * E),
-        # fused: n partial logit matrices read and the scores written; else the scores read
-        "route_topk": ("hbm", (router_fused_splits(cfg) + 1 if router_fused_splits(cfg) else 1) * T * E * 4
-                       + E * 4 + T * k * 8 + T * 8),
+        # algorithmic: the scores [T, E] once, the bias, and idx, w, thresholds written (the split-K
+        # partial logits the fused kernel reads are implementation traffic, not counted)
+        "route_topk": ("hbm", T * E * 4 + E * 4 + T * k * 8 + T * 8),
         "qb_hist": ("hbm", T * E * 4 + E * 4 + T * 8 + E * NB * 4 * 2),
         "gemm_down": ("mfma", 2.0 * T * D * L),
         "perm_count": ("hbm", T * k * 4),
@@ -150,7 +156,16 @@ def cpu_baseline(cfg, inp, sample_tokens: int) -> dict:
     O.permute(idx, cfg.n_experts)
     O.expert_path(sub, cfg_s, idx, w)
     dt = time.perf_counter() - t0
-    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "cpu_model": model, "kind": "oracle",
             "sample": f"first {sample_tokens} tokens of the {cfg.name} batch through the full forward "
                       f"(route, QB histogram, permutation, all touched experts, shared, combine, norm, up): "
                       f"{dt:.1f} s"}
@@ -180,32 +195,29 @@ def mx_work(cfg, offsets) -> dict:
     }
 
 
-def mx_steps(cfg, w, x, args, _lib, torch, LatentMoE) -> dict:
-    """Forward steps with the routed experts on MX operands (MXFP4 weights, MXFP8 activations)."""
+def mx_steps(cfg, w, xs, args, _lib, torch, LatentMoE, flush) -> dict:
+    """Forward steps with the routed experts on MX operands (MXFP4 weights, MXFP8 activations), timed
+    like the headline steps."""
     layer = LatentMoE(cfg, w, mx=True)
 
-    def step():
-        layer.forward(x)
+    def step(i):
+        layer.forward(xs[i % 2])
         layer.qb_update()
 
-    for _ in range(max(args.warmup, 2)):
-        step()
+    for i in range(max(args.warmup, 2)):
+        step(i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    t = timed_steps(step, args.steps, flush, torch, _lib, None)
     bd_steps = min(args.steps, 20)  # per-kernel breakdown in a pass of its own
     _lib.profile_reset()
     _lib.profile_enable(True)
-    for _ in range(bd_steps):
-        step()
+    for i in range(bd_steps):
+        step(i)
     torch.cuda.synchronize()
     _lib.profile_enable(False)
     _lib.profile_collect()
     kernels, roof = {}, {}
-    b = layer.forward(x)
+    b = layer.forward(xs[0])
     torch.cuda.synchronize()
     work = mx_work(cfg, b["offsets"].cpu().numpy())
     for n in MX_KERNELS:
@@ -220,10 +232,9 @@ def mx_steps(cfg, w, x, args, _lib, torch, LatentMoE) -> dict:
         if len(work[n]) > 2:
             tf = work[n][2] / step_s / 1e12
             roof[n].update({"mfma_tflops": round(tf, 1), "mfma_frac_fp8": round(tf / FP8_PEAK_TFLOPS, 4)})
-    ms_step = elapsed / args.steps * 1e3
     del layer
-    return {"ms_per_step": ms_step, "tokens_per_s": cfg.T / (ms_step / 1e3), "kernels_ms_per_step": kernels,
-            "kernels_roofline": roof}
+    return {"ms_per_step": t["ms_median"], "ms_min": t["ms_min"], "tokens_per_s": cfg.T / (t["ms_median"] / 1e3),
+            "kernels_ms_per_step": kernels, "kernels_roofline": roof}
 
 
 BWD_KERNELS = ["bwd_transpose", "bwd_gemm_dn", "bwd_gemm_dw", "bwd_combine_norm", "bwd_dgamma", "bwd_router_dw",
@@ -268,28 +279,200 @@ def train_steps(layer, x, cfg, args, _lib, torch) -> dict:
             "backward_kernels_ms_per_step": kernels, "backward_kernels_sum_ms": round(sum(kernels.values()), 4)}
 
 
-def graph_steps(layer, x, cfg, args, torch) -> dict:
+def graph_steps(layer, xs, cfg, args, torch, flush) -> dict:
     """The same step (forward + QB update) recorded once as a HIP graph and replayed: the launch
-    gaps between the step's kernels go away; the kernels are the same."""
+    gaps between the step's kernels go away; the kernels are the same. The graph reads x from one
+    buffer, into which the two batches are copied in turn (outside the timed replays)."""
     layer.qb_update()  # close the step of the forward that read the offsets
-    g, _ = layer.capture_step(x)
+    xg = xs[0].clone()
+    g, _ = layer.capture_step(xg)
     for _ in range(2):
         g.replay()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
+    stream = torch.cuda.current_stream()
+    times = []
+    for i in range(args.steps):
+        xg.copy_(xs[i % len(xs)])
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         g.replay()
+        e1.record(stream)
+        times.append((e0, e1))
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    ms = sorted(a.elapsed_time(b) for a, b in times)
     del g
-    return {"ms_per_step": ms, "tokens_per_s": cfg.T / (ms / 1e3)}
+    med = ms[len(ms) // 2]
+    return {"ms_per_step": med, "ms_min": ms[0], "tokens_per_s": cfg.T / (med / 1e3)}
+
+
+def make_flush(torch):
+    """A write of 512 MB (twice the 256 MB MALL) that evicts the caches between timed steps."""
+    buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    state = {"v": 0}
+
+    def flush():
+        state["v"] = (state["v"] + 1) & 0xFF
+        buf.fill_(state["v"])
+    return flush
+
+
+def timed_steps(step, n_steps: int, flush, torch, _lib, dominant: str | None) -> dict:
+    """n_steps steps, each preceded by a cache flush and bracketed by HIP events on the launch
+    stream; the dominant kernel's launches are also bracketed by the library's own events."""
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
+    _lib.profile_reset()
+    if dominant:
+        _lib.profile_only(dominant)
+        _lib.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        flush()
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    _lib.profile_enable(False)
+    _lib.profile_collect()
+    _lib.profile_only(None)
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    out = {"ms_median": ms[len(ms) // 2], "ms_min": ms[0], "ms_mean": sum(ms) / len(ms), "wall_s": wall}
+    if dominant:
+        cnt, tot = _lib.profile_get(dominant)
+        out["dominant_avg_ms"] = tot / cnt if cnt else None
+    return out
+
+
+def breakdown(step, n: int, torch, _lib) -> dict:
+    """Per-kernel milliseconds per step: every kernel between HIP events (a pass of its own)."""
+    names = ["router_split", "gemm_router", "route_topk", "qb_hist", "gemm_down", "perm_count", "perm_scan",
+             "perm_scatter", "gather_rows", "mtile_prefix", "gemm_glu_grouped", "gemm_down_grouped",
+             "gemm_glu_dense", "gemm_out_dense", "combine_norm", "gemm_up", "splitk_reduce", "qb_update"]
+    _lib.profile_reset()
+    _lib.profile_enable(True)
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    _lib.profile_enable(False)
+    _lib.profile_collect()
+    out = {}
+    for nm in names:
+        cnt, ms = _lib.profile_get(nm)
+        if cnt:
+            out[nm] = round(ms / n, 4)
+    return out
+
+
+def dominant_roofline(cfg, offsets, avg_ms: float) -> dict:
+    """The routed experts' GEMM1 + SiTU-GLU against both rooflines; `bound` names the binding one
+    (HBM below the ridge intensity, MFMA above it)."""
+    bytes_, flops = glu_bytes(cfg, offsets)
+    gbs = bytes_ / (avg_ms * 1e-3) / 1e9
+    tf = flops / (avg_ms * 1e-3) / 1e12
+    intensity = flops / bytes_
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity < ridge:
+        return {"kernel": DOMINANT, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": bytes_, "avg_launch_ms": round(avg_ms, 4),
+                "mfma_tflops": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                "intensity_flop_per_byte": round(intensity, 1)}
+    return {"kernel": DOMINANT, "bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops, "avg_launch_ms": round(avg_ms, 4),
+            "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "intensity_flop_per_byte": round(intensity, 1)}
+
+
+def k3_weights(cache: dict, torch, upload_weights, make_inputs, K3):
+    """The K3-shape weights, drawn and uploaded once for the three K3 workloads."""
+    from dataclasses import replace
+
+    if "w" not in cache:
+        inp = make_inputs(replace(K3, T=0), with_x=False)
+        cache["inp"] = inp
+        cache["w"] = upload_weights(inp, K3.act_dtype)
+        torch.cuda.synchronize()
+    return cache["inp"], cache["w"]
+
+
+def setup_workload(cfg, cache, torch, np):
+    """(host inputs, device weights, two device batches) of a workload; K3 shapes share weights."""
+    from latent_space_routed_amd import to_device, upload_weights
+    from workloads import CONFIGS
+    from workloads.inputs import logit_offsets, make_inputs, token_rows
+
+    if cfg.d_model == CONFIGS["k3_prefill"].d_model:
+        inp_w, w = k3_weights(cache, torch, upload_weights, make_inputs, CONFIGS["k3_prefill"])
+        inp = dict(inp_w)
+        w = dict(w)
+        off = logit_offsets(cfg)
+        inp["logit_offset"] = off
+        w["logit_offset"] = to_device(off, cfg.act_dtype) if off is not None else None
+    else:
+        inp = make_inputs(cfg, with_x=False)
+        w = upload_weights(inp, cfg.act_dtype)
+    inp["x"] = token_rows(cfg, 0, 0)
+    first = 0 if cfg.qb_updates <= 1 else cfg.qb_updates  # the stress batches after its QB loop
+    xs = [to_device(token_rows(cfg, 0, first + b), cfg.act_dtype) for b in range(2)]
+    return inp, w, xs
+
+
+def qb_loop(layer, cfg, torch, np):
+    """The QB loop over distinct batches, the bias carried forward (untimed), reporting the load."""
+    from latent_space_routed_amd import to_device
+    from workloads.inputs import token_rows
+
+    ratios = []
+    for bt in range(cfg.qb_updates):
+        xb = to_device(token_rows(cfg, 0, bt), cfg.act_dtype)
+        counts = np.diff(layer.forward(xb)["offsets"].cpu().numpy())
+        ratios.append(round(float(counts.max() / counts.mean()), 3))
+        layer.qb_update()
+        del xb
+    return {"updates": cfg.qb_updates, "max_over_mean_expert_load": ratios,
+            "note": "load of each batch's forward, before that batch's bias update"}
+
+
+def run_workload(cfg, args, cache, flush, torch, np, _lib, headline: bool) -> tuple[dict, object, dict, list]:
+    from latent_space_routed_amd import LatentMoE
+
+    log(f"[bench] {cfg.name}: inputs")
+    inp, w, xs = setup_workload(cfg, cache, torch, np)
+    layer = LatentMoE(cfg, w)
+    res = {}
+    if cfg.qb_updates > 1:
+        log(f"[bench] {cfg.name}: {cfg.qb_updates} QB updates over distinct batches")
+        res["qb"] = qb_loop(layer, cfg, torch, np)
+
+    def step(i):
+        layer.forward(xs[i % 2])
+        layer.qb_update()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] {cfg.name}: {args.steps} timed steps")
+    t = timed_steps(step, args.steps, flush, torch, _lib, DOMINANT)
+    b = layer.forward(xs[0])
+    layer.qb_update()
+    torch.cuda.synchronize()
+    offsets = b["offsets"].cpu().numpy()
+    res.update({"T": cfg.T, "ms_per_step": t["ms_median"], "ms_min": t["ms_min"], "ms_mean": t["ms_mean"],
+                "tokens_per_s": cfg.T / (t["ms_median"] / 1e3),
+                "roofline": dominant_roofline(cfg, offsets, t["dominant_avg_ms"]) if t["dominant_avg_ms"] else None})
+    kernels = breakdown(step, min(args.steps, 20), torch, _lib)
+    res["kernels_ms_per_step"] = kernels
+    res["kernels_roofline"] = kernel_roofline(kernel_work(cfg, offsets, layer.fused), kernels)
+    return res, layer, inp, xs
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="k3_prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=2048)
@@ -299,6 +482,8 @@ def main() -> int:
                     help="skip the replays of the step recorded as a HIP graph (reported under 'graph')")
     ap.add_argument("--no-mx", action="store_true",
                     help="skip the forward steps with MX routed experts (reported under 'mx')")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (reported under 'configs')")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB 5 times (counter calibration)")
     args = ap.parse_args()
@@ -309,9 +494,8 @@ def main() -> int:
     import numpy as np
     import torch
 
-    from latent_space_routed_amd import LatentMoE, _lib, to_device, upload_weights
+    from latent_space_routed_amd import LatentMoE, _lib
     from workloads import CONFIGS
-    from workloads.inputs import make_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -334,95 +518,29 @@ def main() -> int:
                           "read_plus_write_GBs": 2 * n / ms / 1e6}), flush=True)
         return 0
     cfg = CONFIGS[args.workload]
-    log(f"[bench] generating {cfg.name} inputs")
-    t0 = time.perf_counter()
-    inp = make_inputs(cfg)
-    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
-    w = upload_weights(inp, cfg.act_dtype)
-    x = to_device(inp["x"], cfg.act_dtype)
-    layer = LatentMoE(cfg, w)
-    torch.cuda.synchronize()
-
-    def step():
-        layer.forward(x)
-        layer.qb_update()
-
-    qb_report = None
-    if cfg.qb_updates > 1:  # the QB loop over distinct batches, the bias carried forward (untimed)
-        from workloads.inputs import token_rows
-
-        log(f"[bench] {cfg.qb_updates} QB updates over batches 0..{cfg.qb_updates - 1}")
-        ratios = []
-        for bt in range(cfg.qb_updates):
-            xb = x if bt == 0 else to_device(token_rows(cfg, 0, bt), cfg.act_dtype)
-            counts = np.diff(layer.forward(xb)["offsets"].cpu().numpy())
-            ratios.append(round(float(counts.max() / counts.mean()), 3))
-            layer.qb_update()
-            del xb
-        qb_report = {"updates": cfg.qb_updates, "max_over_mean_expert_load": ratios,
-                     "note": "load of each batch's forward, before that batch's bias update"}
-
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Timed region: HIP events bracket the dominant kernel only (events around every kernel add
-    # ~0.14 ms to a K3 step); the per-kernel breakdown comes from a second pass below.
-    _lib.profile_reset()
-    _lib.profile_only(DOMINANT)
-    _lib.profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    _lib.profile_enable(False)
-    _lib.profile_collect()
-    _lib.profile_only(None)
-    log(f"[bench] timed {args.steps} steps in {elapsed:.3f} s")
-    cnt, ms = _lib.profile_get(DOMINANT)
-    avg_s = ms / cnt / 1e3
-
-    bd_steps = min(args.steps, 20)  # breakdown pass: every kernel between HIP events
-    _lib.profile_reset()
-    _lib.profile_enable(True)
-    for _ in range(bd_steps):
-        step()
-    torch.cuda.synchronize()
-    _lib.profile_enable(False)
-    _lib.profile_collect()
-
-    names = ["router_split", "gemm_router", "route_topk", "qb_hist", "gemm_down", "perm_count", "perm_scan",
-             "perm_scatter", "gather_rows", "mtile_prefix", "gemm_glu_grouped", "gemm_down_grouped",
-             "gemm_glu_dense", "gemm_out_dense", "combine_norm", "gemm_up", "splitk_reduce", "qb_update"]
-    kernels = {}
-    for n in names:
-        cnt, ms = _lib.profile_get(n)
-        if cnt:
-            kernels[n] = round(ms / bd_steps, 4)
-    b = layer.forward(x)
-    torch.cuda.synchronize()
-    offsets = b["offsets"].cpu().numpy()
-    bytes_, flops = glu_bytes(cfg, offsets)
-    achieved = bytes_ / avg_s / 1e9
+    flush = make_flush(torch)
+    cache = {}
+    head, layer, inp, xs = run_workload(cfg, args, cache, flush, torch, np, _lib, True)
+    roof = dict(head["roofline"])
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("source_digest") == source_digest() and tr.get("workload") == cfg.name:
             traffic = tr.get("bytes_per_launch")
-
-    ms_per_step = elapsed / args.steps * 1e3
+    roof["traffic"] = traffic
     out = {
         "metric": METRIC,
-        "value": cfg.T * args.steps / elapsed,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
+        "ms_per_step_min": head["ms_min"],
+        "ms_per_step_mean": head["ms_mean"],
+        "timing": "median of per-step HIP events; a 512 MB write flushes the MALL before each step, outside "
+                  "the events; two batches alternate; the bias update runs every step",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -431,28 +549,43 @@ def main() -> int:
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d_model, "d_latent": cfg.d_latent,
                    "n_experts": cfg.n_experts, "top_k": cfg.top_k, "inter": cfg.inter, "n_shared": cfg.n_shared,
                    "inter_shared": cfg.inter_shared, "n_bins": cfg.n_bins, "parallelism": "none (1 GPU)"},
-        "roofline": {"kernel": DOMINANT, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes": bytes_, "avg_launch_ms": round(avg_s * 1e3, 4),
-                     "mfma_tflops": round(flops / avg_s / 1e12, 1),
-                     "mfma_frac": round(flops / avg_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
-        "kernels_ms_per_step": kernels,
-        "kernels_note": f"a pass of {bd_steps} steps after the timed region, HIP events around every kernel",
-        "kernels_roofline": kernel_roofline(kernel_work(cfg, offsets, layer.fused), kernels),
+        "roofline": roof,
+        "kernels_ms_per_step": head["kernels_ms_per_step"],
+        "kernels_note": "a pass of its own after the timed region, HIP events around every kernel",
+        "kernels_roofline": head["kernels_roofline"],
     }
-    if qb_report:
-        out["qb"] = qb_report
+    if "qb" in head:
+        out["qb"] = head["qb"]
     if not args.no_graph:
         log("[bench] graph replays")
-        out["graph"] = graph_steps(layer, x, cfg, args, torch)
+        out["graph"] = graph_steps(layer, xs, cfg, args, torch, flush)
     if args.backward:
-        out["train"] = train_steps(layer, x, cfg, args, _lib, torch)
+        out["train"] = train_steps(layer, xs[0], cfg, args, _lib, torch)
+    del layer
+    torch.cuda.empty_cache()
     if not args.no_mx and cfg.act_dtype == "bf16":
         log("[bench] MX routed experts")
-        out["mx"] = mx_steps(cfg, w, x, args, _lib, torch, LatentMoE)
+        _, w_mx, _ = setup_workload(cfg, cache, torch, np)
+        out["mx"] = mx_steps(cfg, w_mx, xs, args, _lib, torch, LatentMoE, flush)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on {min(args.cpu_sample, cfg.T)} tokens")
         out["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_sample, cfg.T))
+    if not args.no_configs:
+        configs = {}
+        for name in ("tiny_f32", "mid_bf16", "k3_decode", "k3_stress"):
+            if name == cfg.name:
+                continue
+            res, lay, _, _ = run_workload(CONFIGS[name], args, cache, flush, torch, np, _lib, False)
+            configs[name] = {k: res[k] for k in ("T", "ms_per_step", "ms_min", "tokens_per_s", "roofline")}
+            configs[name]["dtype"] = CONFIGS[name].act_dtype
+            top = sorted(res["kernels_ms_per_step"].items(), key=lambda kv: -kv[1])[:4]
+            configs[name]["top_kernels_ms"] = dict(top)
+            if "qb" in res:
+                configs[name]["qb"] = res["qb"]
+            del lay
+            torch.cuda.empty_cache()
+        out["configs"] = configs
     print(json.dumps(out), flush=True)
     return 0
 

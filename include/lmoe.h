@@ -74,10 +74,20 @@ size_t lmoe_workspace_bytes(const lmoe_shape* shape, int which_call);
 /* Human-readable name of a status. */
 const char* lmoe_status_string(lmoe_status status);
 
+/* One-time preparation of the router weights for bf16 layers (A1 at f32 accuracy on bf16 MFMA):
+ * w_router [E, D] f32 -> w_router_split [E, 3D] bf16 bits, row e = [hi | mid | lo] with
+ * hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid) (each step one f32 operation), so that
+ * every product x . hi + x . mid + x . lo is exact in f32. Re-run after every weight change.
+ * LMOE_ERR_UNSUPPORTED for f32 layers (their router multiplies the f32 weights directly). */
+lmoe_status lmoe_split_router(const lmoe_shape* shape, const float* w_router, void* w_router_split, void* stream);
+
 /* A1 + A2: router scores, biased top-k selection and combine weights.
  * [slm] 路由机制 (router over x, then top-K); [vxz] 02 (per-expert selection bias, no aux loss).
  *   x            [T, D] act_dtype         token activations
- *   w_router     [E, D] f32               router weights
+ *   w_router     [E, D] f32               router weights (unused when w_router_split is given)
+ *   w_router_split [E, 3D] bf16 or NULL   the split written by lmoe_split_router (bf16 layers only;
+ *                                         NULL: the call splits w_router itself, in the workspace;
+ *                                         LMOE_ERR_INVALID_ARGUMENT if given for an f32 layer)
  *   bias         [E] f32                  quantile-balancing selection bias b
  *   logit_offset [E] f32 or NULL          added to the logits before the sigmoid
  *   scores       [T, E] f32   (out)       s = sigmoid(x . w_router^T + logit_offset)
@@ -85,11 +95,11 @@ const char* lmoe_status_string(lmoe_status status);
  *                                         lower expert index)
  *   topk_w       [T, k] f32   (out)       s of the selected experts divided by their sum
  *   thresh       [T, 2] f32   (out)       k-th and (k+1)-th largest s + b of the row
- *   workspace    LMOE_CALL_ROUTE bytes    (bf16 activations: a three-way bf16 split of w_router so
- *                                         the products are exact and accumulate in f32)          */
-lmoe_status lmoe_route(const lmoe_shape* shape, const void* x, const float* w_router, const float* bias,
-                       const float* logit_offset, float* scores, int32_t* topk_idx, float* topk_w,
-                       float* thresh, void* workspace, size_t workspace_bytes, void* stream);
+ *   workspace    LMOE_CALL_ROUTE bytes    (the per-call split when w_router_split is NULL, and
+ *                                         split-K partial logits of small or half-chip batches)  */
+lmoe_status lmoe_route(const lmoe_shape* shape, const void* x, const float* w_router, const void* w_router_split,
+                       const float* bias, const float* logit_offset, float* scores, int32_t* topk_idx,
+                       float* topk_w, float* thresh, void* workspace, size_t workspace_bytes, void* stream);
 
 /* A3: quantile-balancing histogram ([vxz] 02; [tahou] 负载均衡优化: bin the scores after mapping
  * them to 0..1, and add histograms across micro-batches).
@@ -301,7 +311,9 @@ lmoe_status lmoe_grouped_situ_glu_mx(const lmoe_shape* shape, int32_t n_groups, 
  * per-kernel totals; lmoe_profile_get() reads the totals of kernel `name` (count of launches and
  * summed milliseconds). lmoe_profile_only(name) restricts the timing to the kernels named `name`
  * (NULL: every kernel again), so that a timed region carries only the events it needs; `name` is
- * copied. Host-side state, not thread-safe: a measurement aid only. */
+ * copied. A measurement aid: with timing off (the default) a launch reads one atomic flag and no
+ * other state; with timing on, the process-wide event lists are guarded by a lock, so calls from
+ * several host threads stay safe (their launches are then timed together). */
 void lmoe_profile_enable(int on);
 void lmoe_profile_only(const char* name);
 void lmoe_profile_reset(void);

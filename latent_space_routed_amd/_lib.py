@@ -22,7 +22,7 @@ LMOE_CALL_BWD_UP, LMOE_CALL_BWD_COMBINE_NORM, LMOE_CALL_BWD_EXPERTS, LMOE_CALL_B
     16, 17, 18, 19, 20
 
 # every symbol include/lmoe.h declares
-EXPORTS = ("lmoe_workspace_bytes", "lmoe_status_string", "lmoe_route", "lmoe_qb_histogram", "lmoe_qb_update",
+EXPORTS = ("lmoe_workspace_bytes", "lmoe_status_string", "lmoe_split_router", "lmoe_route", "lmoe_qb_histogram", "lmoe_qb_update",
            "lmoe_permute", "lmoe_grouped_situ_glu", "lmoe_pack_shared", "lmoe_combine_norm_up",
            "lmoe_bwd_transpose_weights", "lmoe_bwd_up", "lmoe_bwd_combine_norm", "lmoe_bwd_router",
            "lmoe_bwd_experts", "lmoe_bwd_down", "lmoe_bwd_shared", "lmoe_mx_quantize", "lmoe_grouped_situ_glu_mx",
@@ -65,7 +65,8 @@ def lib() -> ctypes.CDLL:
         sigs = {
             "lmoe_workspace_bytes": (ctypes.c_size_t, [_S, ctypes.c_int]),
             "lmoe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
-            "lmoe_route": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+            "lmoe_split_router": (ctypes.c_int, [_S, _P, _P, _P]),
+            "lmoe_route": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "lmoe_qb_histogram": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P]),
             "lmoe_qb_update": (ctypes.c_int, [_S, _P, ctypes.c_int64, _P, _P]),
             "lmoe_permute": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -135,10 +136,19 @@ def workspace_bytes(shape: Shape, which: int) -> int:
     return int(lib().lmoe_workspace_bytes(ctypes.byref(shape), which))
 
 
-def lmoe_route(shape, x, w_router, bias, logit_offset, scores, topk_idx, topk_w, thresh, workspace, stream=None):
-    _check("lmoe_route", lib().lmoe_route(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(bias),
-                                          _ptr(logit_offset), _ptr(scores), _ptr(topk_idx), _ptr(topk_w),
-                                          _ptr(thresh), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+def lmoe_split_router(shape, w_router, w_router_split, stream=None):
+    _check("lmoe_split_router", lib().lmoe_split_router(ctypes.byref(shape), _ptr(w_router), _ptr(w_router_split),
+                                                        _stream(stream)))
+
+
+def lmoe_route(shape, x, w_router, bias, logit_offset, scores, topk_idx, topk_w, thresh, workspace, stream=None,
+               w_router_split=None):
+    """w_router_split (optional, bf16 layers): the lmoe_split_router output, so the call does not
+    split the router weights again."""
+    _check("lmoe_route", lib().lmoe_route(ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(w_router_split),
+                                          _ptr(bias), _ptr(logit_offset), _ptr(scores), _ptr(topk_idx),
+                                          _ptr(topk_w), _ptr(thresh), _ptr(workspace), _nbytes(workspace),
+                                          _stream(stream)))
 
 
 def lmoe_qb_histogram(shape, scores, bias, topk_idx, thresh, hist, stream=None):

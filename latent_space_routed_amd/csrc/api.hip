@@ -135,16 +135,28 @@ size_t lmoe_workspace_bytes(const lmoe_shape* sh, int which) {
   }
 }
 
-lmoe_status lmoe_route(const lmoe_shape* sh, const void* x, const float* w_router, const float* bias,
-                       const float* logit_offset, float* scores, int32_t* topk_idx, float* topk_w, float* thresh,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+lmoe_status lmoe_split_router(const lmoe_shape* sh, const float* w_router, void* w_router_split, void* stream) {
+  lmoe_status st = check_shape(sh);
+  if (st != LMOE_OK) return st;
+  if (sh->act_dtype != LMOE_BF16) return LMOE_ERR_UNSUPPORTED;
+  if (!aligned16(w_router) || !aligned16(w_router_split)) return LMOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_split3(w_router, static_cast<uint16_t*>(w_router_split), sh->n_experts, sh->d_model,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+lmoe_status lmoe_route(const lmoe_shape* sh, const void* x, const float* w_router, const void* w_router_split,
+                       const float* bias, const float* logit_offset, float* scores, int32_t* topk_idx, float* topk_w,
+                       float* thresh, void* workspace, size_t workspace_bytes, void* stream) {
   lmoe_status st = check_shape(sh);
   if (st != LMOE_OK) return st;
   if (sh->T == 0) return LMOE_OK;
-  if (!aligned16(x) || !aligned16(w_router) || !aligned4(bias) || !aligned16(scores) || !aligned4(topk_idx) ||
-      !aligned4(topk_w) || !aligned4(thresh) || (logit_offset && !aligned4(logit_offset)))
+  const bool presplit = sh->act_dtype == LMOE_BF16 && w_router_split != nullptr;
+  if (!aligned16(x) || !(presplit ? aligned16(w_router_split) : aligned16(w_router)) || !aligned4(bias) ||
+      !aligned16(scores) || !aligned4(topk_idx) || !aligned4(topk_w) || !aligned4(thresh) ||
+      (logit_offset && !aligned4(logit_offset)))
     return LMOE_ERR_INVALID_ARGUMENT;
-  const size_t need = route_ws(sh);
+  if (sh->act_dtype != LMOE_BF16 && w_router_split) return LMOE_ERR_INVALID_ARGUMENT;
+  const size_t need = presplit ? 0 : route_ws(sh);
   if (need && (!workspace || workspace_bytes < need || !aligned16(workspace))) return LMOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int T = sh->T, D = sh->d_model, E = sh->n_experts;
@@ -160,9 +172,13 @@ lmoe_status lmoe_route(const lmoe_shape* sh, const void* x, const float* w_route
   a.col_bias = logit_offset;
   a.tag = "gemm_router";
   if (sh->act_dtype == LMOE_BF16) {
-    uint16_t* wsplit = static_cast<uint16_t*>(workspace);
-    st = hip_status(launch_split3(w_router, wsplit, E, D, s));
-    if (st != LMOE_OK) return st;
+    const uint16_t* wsplit = static_cast<const uint16_t*>(w_router_split);
+    if (!presplit) {  // the three-part split of this call's weights, in the workspace
+      uint16_t* tmp = static_cast<uint16_t*>(workspace);
+      st = hip_status(launch_split3(w_router, tmp, E, D, s));
+      if (st != LMOE_OK) return st;
+      wsplit = tmp;
+    }
     a.B = wsplit;
     a.ldb = 3 * (int64_t)D;
     a.K = 3 * D;

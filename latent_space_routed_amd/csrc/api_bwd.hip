@@ -40,7 +40,7 @@ size_t ws_combine(const lmoe_shape* sh) {  // block partials of dgamma and their
   return round_up((blocks + (blocks + 63) / 64) * sh->d_latent * sizeof(float));
 }
 size_t ws_experts(const lmoe_shape* sh) {
-  const size_t idx = 2 * round_up((size_t)(sh->n_experts + 1) * 4);
+  const size_t idx = 3 * round_up((size_t)(sh->n_experts + 1) * 4);
   const size_t rows = (size_t)(sh->d_latent + sh->inter + 2 * sh->inter + sh->d_latent);
   return idx + round_up(rows * kpad(sh) * esize(sh->act_dtype));
 }
@@ -219,16 +219,23 @@ lmoe_status lmoe_bwd_experts(const lmoe_shape* sh, const void* x_lat, const int3
   const size_t ia = round_up((size_t)(E + 1) * 4);
   int32_t* mts = reinterpret_cast<int32_t*>(ws);                // m-tile prefix of the grouped GEMMs
   int32_t* ptile = reinterpret_cast<int32_t*>(ws + ia);         // 64-row tile prefix (padded K ranges)
-  char* tb = ws + 2 * ia;
+  int32_t* mts_kn = reinterpret_cast<int32_t*>(ws + 2 * ia);    // m-tile prefix of the [K, N]-B GEMMs
+  char* tb = ws + 3 * ia;
   void* dy_t = tb;                                       // [L, Kp]
   void* h_t = tb + (size_t)L * Kp * esz;                 // [I, Kp]
   void* dgu_t = tb + (size_t)(L + I) * Kp * esz;         // [2I, Kp]
   void* xp_t = tb + (size_t)(L + 3 * I) * Kp * esz;      // [L, Kp]
   // with no rows every K-range is empty and the K-grouped GEMMs write zero gradients
   const GemmShape gshape = (int64_t)rows >= (int64_t)E * 64 ? GemmShape::Big : GemmShape::Small;
+  // The products that read W2_e and W1_e in place as [K, N] run on the 256-row DMA pipeline for bf16
+  // only; f32 takes 128-row register tiles, and the m-tile numbering must follow the tile launched.
+  const GemmShape kn_shape = dt == LMOE_BF16 ? gshape : GemmShape::Small;
   st = hip_status(launch_mtile_prefix(expert_offsets, E, gemm_block_m(gshape), mts, s));
   if (st == LMOE_OK) st = hip_status(launch_mtile_prefix(expert_offsets, E, 64, ptile, s));
+  if (st == LMOE_OK && kn_shape != gshape)
+    st = hip_status(launch_mtile_prefix(expert_offsets, E, gemm_block_m(kn_shape), mts_kn, s));
   if (st != LMOE_OK) return st;
+  const int32_t* kn_mts = kn_shape != gshape ? mts_kn : mts;
   auto grouped = [&](const void* A, int64_t lda, const void* B, int64_t ldb, int64_t bstride, void* C, int64_t ldc,
                      int N, int K, const char* tag) {
     GemmArgs a = gargs(sh);
@@ -274,7 +281,8 @@ lmoe_status lmoe_bwd_experts(const lmoe_shape* sh, const void* x_lat, const int3
   if (rows > 0) {
     GemmArgs a = grouped(dy_perm, L, w2, I, (int64_t)L * I, dh, I, I, L, "bwd_gemm_dh");
     a.b_kn = true;
-    st = hip_status(launch_gemm(a, dt, Epi::Store, dt == LMOE_BF16 ? gshape : GemmShape::Small, s));
+    a.mtile_start = kn_mts;
+    st = hip_status(launch_gemm(a, dt, Epi::Store, kn_shape, s));
   }
   // dW2_e = dy_e^T h_e
   if (st == LMOE_OK)
@@ -298,7 +306,8 @@ lmoe_status lmoe_bwd_experts(const lmoe_shape* sh, const void* x_lat, const int3
   if (st == LMOE_OK && rows > 0) {
     GemmArgs a = grouped(dgu, 2 * I, w1, L, (int64_t)2 * I * L, dx_perm, L, L, 2 * I, "bwd_gemm_dx_experts");
     a.b_kn = true;
-    st = hip_status(launch_gemm(a, dt, Epi::Store, dt == LMOE_BF16 ? gshape : GemmShape::Small, s));
+    a.mtile_start = kn_mts;
+    st = hip_status(launch_gemm(a, dt, Epi::Store, kn_shape, s));
   }
   // dW1_e = d[g | u]_e^T x_perm_e (x_perm gathered from x_lat through sorted_token)
   if (st == LMOE_OK)

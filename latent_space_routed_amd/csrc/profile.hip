@@ -1,5 +1,9 @@
 // Optional per-kernel timing with HIP events recorded on the launch stream (a measurement aid).
+// With timing off (the default) a launch reads one atomic flag and touches no other state; with
+// timing on, the event lists are guarded by one lock, so host threads may launch concurrently.
+#include <atomic>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -17,7 +21,8 @@ struct Total {
   double ms = 0.0;
 };
 
-bool g_enabled = false;
+std::atomic<bool> g_enabled{false};
+std::mutex g_mu;     // guards everything below
 std::string g_only;  // when not empty, the one kernel name that is timed
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_pool;
@@ -37,7 +42,8 @@ hipEvent_t take_event() {
 }  // namespace
 
 KernelTimer::KernelTimer(const char* n, hipStream_t s) : name(n), stream(s), ev0(nullptr) {
-  if (!g_enabled) return;
+  if (!g_enabled.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_mu);
   if (!g_only.empty() && (n == nullptr || g_only != n)) return;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;  // no timing events inside a graph capture
   if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
@@ -47,6 +53,7 @@ KernelTimer::KernelTimer(const char* n, hipStream_t s) : name(n), stream(s), ev0
 
 KernelTimer::~KernelTimer() {
   if (!ev0) return;
+  std::lock_guard<std::mutex> lk(g_mu);
   hipEvent_t e = take_event();
   if (e && hipEventRecord(e, stream) == hipSuccess) {
     g_pending.push_back({name, static_cast<hipEvent_t>(ev0), e});
@@ -60,13 +67,20 @@ KernelTimer::~KernelTimer() {
 
 extern "C" {
 
-void lmoe_profile_enable(int on) { lmoe::g_enabled = on != 0; }
+void lmoe_profile_enable(int on) { lmoe::g_enabled.store(on != 0, std::memory_order_relaxed); }
 
-void lmoe_profile_only(const char* name) { lmoe::g_only = name ? name : ""; }
+void lmoe_profile_only(const char* name) {
+  std::lock_guard<std::mutex> lk(lmoe::g_mu);
+  lmoe::g_only = name ? name : "";
+}
 
-void lmoe_profile_reset(void) { lmoe::g_totals.clear(); }
+void lmoe_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(lmoe::g_mu);
+  lmoe::g_totals.clear();
+}
 
 lmoe_status lmoe_profile_collect(void) {
+  std::lock_guard<std::mutex> lk(lmoe::g_mu);
   lmoe_status st = LMOE_OK;
   for (auto& p : lmoe::g_pending) {
     float ms = 0.0f;
@@ -86,6 +100,7 @@ lmoe_status lmoe_profile_collect(void) {
 
 int lmoe_profile_get(const char* name, int64_t* launches, double* total_ms) {
   if (!name) return 0;
+  std::lock_guard<std::mutex> lk(lmoe::g_mu);
   auto it = lmoe::g_totals.find(name);
   if (it == lmoe::g_totals.end()) return 0;
   if (launches) *launches = it->second.launches;

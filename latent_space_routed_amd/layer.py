@@ -61,6 +61,11 @@ class LatentMoE:
         self.w2s_packed = torch.empty(D, S * Is, dtype=dt, device=device)
         if S > 0:
             C.lmoe_pack_shared(shape, weights["w1s"], weights["w2s"], self.w1s_packed, self.w2s_packed)
+        # bf16 layers: the router weights split into three bf16 parts once, not per forward
+        self.w_router_split = None
+        if cfg.act_dtype == "bf16":
+            self.w_router_split = torch.empty(E, 3 * D, dtype=torch.bfloat16, device=device)
+            C.lmoe_split_router(shape, weights["w_router"], self.w_router_split)
         if mx:
             self.mx_w = {}
             for name in ("w1", "w2"):
@@ -129,7 +134,7 @@ class LatentMoE:
         E, k, L, D, I = cfg.n_experts, cfg.top_k, cfg.d_latent, cfg.d_model, cfg.inter
         S, Is = cfg.n_shared, cfg.inter_shared
         C.lmoe_route(shape, x, w["w_router"], self.bias, w.get("logit_offset"), b["scores"], b["idx"], b["w"],
-                     b["thresh"], b["ws_route"])
+                     b["thresh"], b["ws_route"], w_router_split=self.w_router_split)
         if accumulate_hist:
             C.lmoe_qb_histogram(shape, b["scores"], self.bias, b["idx"], b["thresh"], self.hist)
             self.n_acc += T

@@ -29,8 +29,8 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 
 @functools.lru_cache(maxsize=4)
-def cached_inputs(cfg, seed: int = 0, batch: int = 0):
-    return make_inputs(cfg, seed=seed, batch=batch)
+def cached_inputs(cfg, seed: int = 0, batch: int = 0, gain_bias: bool = False):
+    return make_inputs(cfg, seed=seed, batch=batch, gain_bias=gain_bias)
 
 
 def device_layer(cfg, inp: dict, max_tokens=None, fused: bool = True) -> tuple[LatentMoE, torch.Tensor]:

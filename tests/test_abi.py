@@ -84,7 +84,9 @@ def test_shape_validation_before_any_launch(lib, field, value, status):
     sh = C.make_shape(CONFIGS["k3_prefill"])
     setattr(sh, field, value)
     null = None
-    assert lib.lmoe_route(ctypes.byref(sh), null, null, null, null, null, null, null, null, null, 0, null) == status
+    assert lib.lmoe_route(ctypes.byref(sh), null, null, null, null, null, null, null, null, null, null, 0, null) == \
+        status
+    assert lib.lmoe_split_router(ctypes.byref(sh), null, null, null) == status
     assert lib.lmoe_qb_histogram(ctypes.byref(sh), null, null, null, null, null, null) == status
     assert lib.lmoe_qb_update(ctypes.byref(sh), null, 1, null, null) == status
 
@@ -98,8 +100,18 @@ def test_pointer_validation_before_any_launch(lib):
     assert lib.lmoe_qb_histogram(ctypes.byref(sh), misaligned, fake, fake, fake, fake, null) == \
         C.LMOE_ERR_INVALID_ARGUMENT
     # route with every pointer plausible but no workspace -> workspace error, still no launch
-    assert lib.lmoe_route(ctypes.byref(sh), fake, fake, fake, null, fake, fake, fake, fake, null, 0, null) == \
+    assert lib.lmoe_route(ctypes.byref(sh), fake, fake, null, fake, null, fake, fake, fake, fake, null, 0, null) == \
         C.LMOE_ERR_WORKSPACE
+    # with the router weights split beforehand the call needs no workspace at T = 8192 (its split-K
+    # partials are optional): validation passes; the misaligned split is rejected first here
+    assert lib.lmoe_route(ctypes.byref(sh), fake, null, misaligned, fake, null, fake, fake, fake, fake, null, 0,
+                          null) == C.LMOE_ERR_INVALID_ARGUMENT
+    # the split is a bf16-layer call; an f32 layer given a split is an error
+    f32 = C.make_shape(CONFIGS["tiny_f32"])
+    assert lib.lmoe_split_router(ctypes.byref(f32), fake, fake, null) == C.LMOE_ERR_UNSUPPORTED
+    assert lib.lmoe_split_router(ctypes.byref(sh), fake, misaligned, null) == C.LMOE_ERR_INVALID_ARGUMENT
+    assert lib.lmoe_route(ctypes.byref(f32), fake, fake, fake, fake, null, fake, fake, fake, fake, fake, 1 << 20,
+                          null) == C.LMOE_ERR_INVALID_ARGUMENT
     # grouped GLU: a row gather needs a_rows consistent; K not a multiple of 64 is unsupported
     assert lib.lmoe_grouped_situ_glu(ctypes.byref(sh), 1, 16, 100, 64, 64, fake, 16, null, null, fake, fake, fake,
                                      fake, 0, null, 0, null) == C.LMOE_ERR_UNSUPPORTED
@@ -113,7 +125,8 @@ def test_pointer_validation_before_any_launch(lib):
 def test_empty_batch_is_a_no_op(lib):
     sh = C.make_shape(CONFIGS["k3_prefill"], T=0)
     null = None
-    assert lib.lmoe_route(ctypes.byref(sh), null, null, null, null, null, null, null, null, null, 0, null) == C.LMOE_OK
+    assert lib.lmoe_route(ctypes.byref(sh), null, null, null, null, null, null, null, null, null, null, 0, null) == \
+        C.LMOE_OK
     assert lib.lmoe_qb_histogram(ctypes.byref(sh), null, null, null, null, null, null) == C.LMOE_OK
     assert lib.lmoe_combine_norm_up(ctypes.byref(sh), null, null, null, null, null, null, null, null, null, null, 0,
                                     null, 0, null) == C.LMOE_OK
@@ -125,9 +138,9 @@ def test_backward_workspace_and_validation(lib):
     for which in (C.LMOE_CALL_BWD_UP, C.LMOE_CALL_BWD_COMBINE_NORM, C.LMOE_CALL_BWD_EXPERTS, C.LMOE_CALL_BWD_DOWN,
                   C.LMOE_CALL_BWD_SHARED):
         assert C.workspace_bytes(k3, which) > 0
-    # experts: two tile prefixes, then [L + I + 2I + L] x (T*k + 64 E) transposed activations
+    # experts: three tile prefixes, then [L + I + 2I + L] x (T*k + 64 E) transposed activations
     kp = 8192 * 16 + 64 * 896
-    assert C.workspace_bytes(k3, C.LMOE_CALL_BWD_EXPERTS) == 2 * 3840 + (3584 * 2 + 3 * 512) * kp * 2
+    assert C.workspace_bytes(k3, C.LMOE_CALL_BWD_EXPERTS) == 3 * 3840 + (3584 * 2 + 3 * 512) * kp * 2
     big = C.make_shape(CONFIGS["k3_prefill"])
     big.d_latent = 4096 + 64                                   # past the combine backward row limit (bf16)
     null = None

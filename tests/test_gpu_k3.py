@@ -1,12 +1,15 @@
 """GPU parity at the K3 layer shape (d_model 7168, d_latent 3584, 896 experts top-16, 2 shared).
 
-* k3_prefill (T=8192), in the launch configuration the benchmark times: routing, histogram, bias
-  update and permutation are checked on every token (bit-exact given the GPU's scores); the
-  expert path on sampled tokens the oracle evaluates one by one.
+* k3_prefill (T=8192), in the launch configuration the benchmark times, with a non-unit RMSNorm
+  gain and a non-zero starting bias: routing, histogram, bias update and permutation are checked
+  on every token (bit-exact given the GPU's scores); the expert path on 1024 seeded-sampled
+  tokens plus every token whose oracle gap between the k-th and (k+1)-th biased score is below
+  1e-5, each evaluated by the oracle one by one.
 * k3_decode (T=64): every token end to end (about 613 of 896 experts touched).
 * k3_stress (T=32768, Zipf(1.1) logit offsets, 0.1% of x entries x50): 8 batches with a bias update
   after each, every step bit-exact given the GPU's scores and histogram, the load spread
-  reported; sampled outputs on the last batch include the tokens carrying the most outliers.
+  reported; the expert path on the last batch is checked on 1024 sampled tokens plus the 64
+  tokens carrying the most outliers and every near-tie token.
 """
 from dataclasses import replace
 
@@ -17,7 +20,7 @@ import torch
 from latent_space_routed_amd import LatentMoE, to_device, upload_weights
 from oracle import lmoe_oracle as O
 from workloads import CONFIGS
-from workloads.inputs import bf16_bits_to_f32, logit_offsets, make_inputs, token_rows
+from workloads.inputs import bf16_bits_to_f32, gain_and_bias, logit_offsets, make_inputs, token_rows
 
 from .gpu_helpers import assert_close_rows, assert_out_parity, host, near_ties, say
 
@@ -37,13 +40,27 @@ def k3_weights():
     return _CACHE["inp"], _CACHE["w"]
 
 
-def layer_for(cfg, fused: bool = True):
+N_SAMPLE = 1024  # seeded-sampled tokens of the expert-path checks at K3 scale
+
+
+def layer_for(cfg, fused: bool = True, gain_bias: bool = False):
     inp_w, w = k3_weights()
     inp = dict(inp_w)
     inp["logit_offset"] = logit_offsets(cfg)
     w = dict(w)
     w["logit_offset"] = to_device(inp["logit_offset"], cfg.act_dtype)
+    if gain_bias:  # gamma = 1 + 0.5 N(0,1), b = 0.05 N(0,1)
+        inp["gamma"], inp["bias"] = gain_and_bias(cfg)
+        w["gamma"] = to_device(inp["gamma"], "f32")
+        w["bias"] = to_device(inp["bias"], "f32")
     return inp, LatentMoE(cfg, w, fused=fused)
+
+
+def sample_tokens(T: int, seed: int, *must) -> np.ndarray:
+    """N_SAMPLE seeded tokens, the first and last token, and every token listed in ``must``."""
+    rng = np.random.default_rng(seed)
+    extra = [np.asarray(m, dtype=np.int64).ravel() for m in must]
+    return np.unique(np.concatenate([rng.choice(T, N_SAMPLE, replace=False), [0, T - 1], *extra]))
 
 
 def check_sampled_tokens(cfg, inp, b, tokens, what):
@@ -109,7 +126,7 @@ def check_routing_all_tokens(cfg, inp, x_host, b, bias):
 
 def test_k3_prefill():
     cfg = K3
-    inp, layer = layer_for(cfg)
+    inp, layer = layer_for(cfg, gain_bias=True)
     x_host = token_rows(cfg)
     inp["x"] = x_host
     x = to_device(x_host, cfg.act_dtype)
@@ -134,8 +151,8 @@ def test_k3_prefill():
     say(f"[k3_prefill] max |s_gpu - s_oracle| = {ds:.2e}; near-tie tokens {int(tie.sum())}; "
         f"differing top-k sets {int((~same).sum())}")
     assert ds <= 2e-6 and np.all(same | tie)
-    rng = np.random.default_rng(0)
-    tokens = np.sort(np.concatenate([rng.choice(cfg.T, 96, replace=False), [0, cfg.T - 1]]))
+    tokens = sample_tokens(cfg.T, 0, np.nonzero(tie)[0])
+    say(f"[k3_prefill] expert path on {len(tokens)} tokens ({int(tie.sum())} near-tie tokens included)")
     check_sampled_tokens(cfg, inp, b, tokens, "k3_prefill")
 
 
@@ -150,8 +167,10 @@ def test_k3_prefill_unfused():
     b = layer.forward(to_device(x_host, cfg.act_dtype))
     torch.cuda.synchronize()
     check_routing_all_tokens(cfg, inp, x_host, b, inp["bias"])
-    rng = np.random.default_rng(1)
-    tokens = np.sort(np.concatenate([rng.choice(cfg.T, 32, replace=False), [cfg.T - 1]]))
+    s_ref = O.router_scores(O.to_f64(x_host, cfg.act_dtype), inp["w_router"], inp["logit_offset"])
+    tie = near_ties(O.select_topk(s_ref, inp["bias"], cfg.top_k)[2])
+    tokens = sample_tokens(cfg.T, 1, np.nonzero(tie)[0])
+    say(f"[k3_prefill unfused] expert path on {len(tokens)} tokens ({int(tie.sum())} near-tie tokens included)")
     check_sampled_tokens(cfg, inp, b, tokens, "k3_prefill unfused")
 
 
@@ -186,19 +205,28 @@ def test_k3_stress_qb_updates():
         if batch == cfg.qb_updates - 1:
             inp["x"] = x_host
             inp["bias"] = bias_before
-            # router on a sample incl. the tokens with the most outlier entries
-            big = (np.abs(bf16_bits_to_f32(x_host)) > 20).sum(axis=1)
-            heavy = np.argsort(-big, kind="stable")[:16]
-            rng = np.random.default_rng(1)
-            tokens = np.unique(np.concatenate([heavy, rng.choice(cfg.T, 48, replace=False)]))
-            s_ref = O.router_scores(O.to_f64(x_host[tokens], cfg.act_dtype), inp["w_router"], inp["logit_offset"])
-            ds = float(np.abs(s[tokens] - s_ref).max())
+            # the oracle's router on every token; the expert path on a sample that holds the tokens
+            # with the most outlier entries and every near-tie token
+            xf = O.to_f64(x_host, cfg.act_dtype)
+            s_ref = O.router_scores(xf, inp["w_router"], inp["logit_offset"])
             idx_ref, _, thr_ref = O.select_topk(s_ref, bias_before, cfg.top_k)
-            same = np.array([set(a) == set(c) for a, c in zip(idx[tokens], idx_ref)])
-            say(f"[k3_stress] router max |s_gpu - s_oracle| on {len(tokens)} tokens = {ds:.2e}; "
-                f"differing top-k sets {int((~same).sum())} (near-ties {int(near_ties(thr_ref).sum())})")
-            # fp32 accumulation of outlier-heavy rows: score error stays inside the tie window
-            assert ds <= 1e-5 and np.all(same | near_ties(thr_ref))
+            tie = near_ties(thr_ref)
+            same = np.array([set(a) == set(c) for a, c in zip(idx, idx_ref)])
+            # Rows carrying x50 outliers have products up to ~50x those of Gaussian rows, and the f32
+            # accumulation error of their logits follows the partial sums those products leave: the
+            # score error is held to the 1e-5 window of the near-tie rule itself (Gaussian rows stay
+            # under 2e-6, checked at prefill), on every token, and any top-k set that differs from
+            # the oracle's must belong to a near-tie token.
+            err = np.abs(s - s_ref)
+            say(f"[k3_stress] router on all {cfg.T} tokens: max |s_gpu - s_oracle| = {err.max():.2e} "
+                f"(99.9th percentile {np.quantile(err, 0.999):.2e}); differing top-k sets {int((~same).sum())} "
+                f"(all near-ties: {bool(np.all(same | tie))}), near-ties {int(tie.sum())}")
+            assert err.max() <= 1e-5 and np.all(same | tie)
+            big = (np.abs(bf16_bits_to_f32(x_host)) > 20).sum(axis=1)
+            heavy = np.argsort(-big, kind="stable")[:64]
+            tokens = sample_tokens(cfg.T, 1, heavy, np.nonzero(tie)[0])
+            say(f"[k3_stress] expert path on {len(tokens)} tokens (64 outlier-heaviest, "
+                f"{int(tie.sum())} near-tie tokens included)")
             check_sampled_tokens(cfg, inp, b, tokens, "k3_stress")
         layer.qb_update()
         want, _ = O.qb_update(hist, cfg.T, bias_before, cfg.top_k)

@@ -1,7 +1,9 @@
 """GPU parity of every C-ABI call and of the whole layer against the CPU oracle (small workloads).
 
-Sizes span several tiles plus ragged tails: tiny_f32 (T=64), mid_bf16 (T=4096), and ragged token
-counts. Integer results (top-k given the scores, histograms, bias updates, permutation) must be
+Sizes span several tiles plus ragged tails: tiny_f32 (T=64), mid_bf16 (T=4096), ragged token
+counts, and tiny_f32 at T=1024 (4096 expert rows: the routed GEMMs take the 256-row DMA pipeline in
+f32). The "_gb" cases draw a non-unit RMSNorm gain and a non-zero starting bias. Integer results
+(top-k given the scores, histograms, bias updates, permutation) must be
 bit-exact; stored floating tensors match to one rounding step of their storage type; the layer
 output matches within 2e-2 x RMS (bf16) or 1e-4 x RMS (f32), excluding only near-tie tokens whose
 top-k set legitimately differs (counted), and within the same bound on every token when the GPU's
@@ -24,11 +26,14 @@ pytestmark = pytest.mark.gpu
 
 TINY = CONFIGS["tiny_f32"]
 MID = CONFIGS["mid_bf16"]
-SMALL_CASES = [TINY, replace(TINY, name="tiny_ragged", T=77), MID, replace(MID, name="mid_ragged", T=1000)]
+# (config, gain_bias): gain_bias draws gamma = 1 + 0.5 N(0,1) and b = 0.05 N(0,1)
+SMALL_CASES = [(TINY, False), (replace(TINY, name="tiny_gb"), True), (replace(TINY, name="tiny_ragged_gb", T=77), True),
+               (replace(TINY, name="tiny_big_gb", T=1024), True), (MID, False),
+               (replace(MID, name="mid_ragged_gb", T=1000), True)]
 # fused: routed GEMM gathers x_lat rows, shared down-projection folded into the up-projection;
 # unfused: x_perm and y_sh materialised
-RUNS = [(c, f) for c in SMALL_CASES for f in (True, False)]
-IDS = [f"{c.name}-{'fused' if f else 'unfused'}" for c, f in RUNS]
+RUNS = [(c, gb, f) for c, gb in SMALL_CASES for f in (True, False)]
+IDS = [f"{c.name}-{'fused' if f else 'unfused'}" for c, gb, f in RUNS]
 _ORACLE = {}
 
 
@@ -40,9 +45,9 @@ def oracle_forward(cfg, inp):
 
 @pytest.fixture(scope="module", params=RUNS, ids=IDS)
 def run(request):
-    cfg, fused = request.param
-    say(f"[case] {cfg.name} T={cfg.T} fused={fused}")
-    inp = cached_inputs(cfg)
+    cfg, gain_bias, fused = request.param
+    say(f"[case] {cfg.name} T={cfg.T} fused={fused} gain_bias={gain_bias}")
+    inp = cached_inputs(cfg, gain_bias=gain_bias)
     layer, x = device_layer(cfg, inp, fused=fused)
     b = layer.forward(x)
     torch.cuda.synchronize()

@@ -55,6 +55,97 @@ def test_bf16_rounding_is_nearest_even_from_float64_brute_force():
     assert O.round_to_bf16(np.array([1.0 + 2.0 ** -8 + 2.0 ** -40]))[0] == 1.0 + 2.0 ** -7
 
 
+def _bf16_from_fields(bits: int) -> float:
+    """The value of a bfloat16 bit pattern written out from its fields: sign bit 15, 8-bit exponent
+    (bias 127), 7-bit fraction; exponent 0 is subnormal (2^-126 * f/128), 255 is inf/NaN."""
+    sign = -1.0 if bits >> 15 else 1.0
+    e, f = (bits >> 7) & 0xFF, bits & 0x7F
+    if e == 0xFF:
+        return sign * math.inf if f == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(f, -126 - 7)
+    return sign * math.ldexp(128 + f, e - 127 - 7)
+
+
+def test_bf16_bits_decode_from_fields():
+    # every finite bit pattern, against the field formula
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns
+        got = O.bf16_bits_to_f64(bits)
+    want = np.array([_bf16_from_fields(int(b)) for b in bits])
+    finite = np.isfinite(want)
+    np.testing.assert_array_equal(got[finite], want[finite])
+    assert np.array_equal(np.isinf(got), np.isinf(want)) and np.array_equal(np.isnan(got), np.isnan(want))
+    # worked values
+    assert O.bf16_bits_to_f64(np.uint16([0x3F80, 0xC000, 0x3F81, 0x0001, 0x7F7F]))[:5].tolist() == [
+        1.0, -2.0, 1.0 + 2.0 ** -7, 2.0 ** -133, (2.0 - 2.0 ** -7) * 2.0 ** 127]
+
+
+def _exact_round_bf16(v) -> float:
+    """Round an exact rational to the nearest bfloat16 (ties to an even significand), in rational
+    arithmetic: with 2^e <= |v| < 2^(e+1), the spacing of bfloat16 values there is 2^(e-7)."""
+    from fractions import Fraction
+
+    v = Fraction(v)
+    if v == 0:
+        return 0.0
+    a = abs(v)
+    e = math.floor(math.log2(a))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = Fraction(2) ** (max(e, -126) - 7)
+    n, r = divmod(a, q)
+    if r * 2 > q or (r * 2 == q and n % 2 == 1):
+        n += 1
+    return math.copysign(float(n * q), v)
+
+
+def _bf16_matrix(rng, shape, scale):
+    from workloads.inputs import f32_to_bf16_bits
+
+    return f32_to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+def test_down_projection_against_exact_sums():
+    # x_lat[t, l] = sum_d x[t, d] W_dn[l, d], each sum formed exactly (rationals), then rounded once
+    # to bfloat16; the oracle must give the same bits
+    from fractions import Fraction
+
+    rng = np.random.default_rng(21)
+    T, D, L = 6, 40, 5
+    x, w = _bf16_matrix(rng, (T, D), 1.0), _bf16_matrix(rng, (L, D), 1.0 / np.sqrt(D))
+    xf, wf = O.bf16_bits_to_f64(x), O.bf16_bits_to_f64(w)
+    got = O.down_project(xf, wf, "bf16")
+    for t in range(T):
+        for l in range(L):
+            exact = sum(Fraction(float(xf[t, d])) * Fraction(float(wf[l, d])) for d in range(D))
+            assert got[t, l] == _exact_round_bf16(exact), (t, l)
+    # f32 storage: the same sums rounded to float32
+    got32 = O.down_project(xf, wf, "f32")
+    want32 = np.array([[float(np.float32(math.fsum(xf[t] * wf[l]))) for l in range(L)] for t in range(T)])
+    np.testing.assert_array_equal(got32, want32)
+
+
+def test_up_projection_against_explicit_sums():
+    # out = n . W_up^T + y_sh per element with math.fsum over the products and the shared term; the
+    # stored value is that sum rounded once to the storage type
+    rng = np.random.default_rng(22)
+    T, L, D = 5, 32, 7
+    n, w = _bf16_matrix(rng, (T, L), 1.0), _bf16_matrix(rng, (D, L), 1.0 / np.sqrt(L))
+    nf, wf = O.bf16_bits_to_f64(n), O.bf16_bits_to_f64(w)
+    ysh = rng.standard_normal((T, D)).astype(np.float32).astype(np.float64)
+    pre, stored = O.up_project(nf, wf, ysh, "bf16")
+    want = np.array([[math.fsum(list(nf[t] * wf[d]) + [ysh[t, d]]) for d in range(D)] for t in range(T)])
+    np.testing.assert_allclose(pre, want, rtol=1e-14, atol=0)
+    np.testing.assert_array_equal(stored, [[_exact_round_bf16(v) for v in row] for row in pre])
+    # without a shared part the products alone; a transposed W_up would not even have this shape
+    pre0, _ = O.up_project(nf, wf, None, "f32")
+    np.testing.assert_allclose(pre0, want - ysh, rtol=1e-13, atol=1e-15)
+    assert pre0.shape == (T, D)
+
+
 # ------------------------------------------------------------------------------------------------
 # elementwise functions
 # ------------------------------------------------------------------------------------------------

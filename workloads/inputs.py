@@ -10,7 +10,8 @@ of the method's arithmetic. Recipe (the pages publish no dataset and no trained 
 * the router weight, bias, logit offsets and gamma are float32; everything else is stored as
   bfloat16 (round-to-nearest-even of the float32 draw, kept as uint16 bit patterns) or float32
   for ``act_dtype == "f32"``;
-* bias b = 0 and gamma = 1 at the start;
+* bias b = 0 and gamma = 1 at the start, or, with ``gain_bias=True`` (parity tests of the gain and
+  of a moved bias), gamma = 1 + 0.5 N(0, 1) and b = 0.05 N(0, 1), each from its own stream;
 * optional skew: logit offsets o_e = -s * ln(r_e) with r a seeded permutation of 1..E (a Zipf(s)
   preference over experts);
 * optional outliers: a Bernoulli(frac) mask of x entries multiplied by ``outlier_scale`` before
@@ -25,7 +26,7 @@ import numpy as np
 
 from .configs import LayerConfig
 
-TID_X, TID_WR, TID_WDN, TID_W1, TID_W2, TID_WUP, TID_W1S, TID_W2S, TID_ZIPF, TID_OUTLIER = range(10)
+TID_X, TID_WR, TID_WDN, TID_W1, TID_W2, TID_WUP, TID_W1S, TID_W2S, TID_ZIPF, TID_OUTLIER, TID_GAMMA, TID_BIAS = range(12)
 X_CHUNK_ROWS = 256
 
 
@@ -105,7 +106,15 @@ def logit_offsets(cfg: LayerConfig, seed: int = 0) -> np.ndarray | None:
     return (-cfg.zipf_s * np.log(r)).astype(np.float32)
 
 
-def make_inputs(cfg: LayerConfig, seed: int = 0, batch: int = 0, with_x: bool = True) -> dict:
+def gain_and_bias(cfg: LayerConfig, seed: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """A non-unit RMSNorm gain gamma = 1 + 0.5 N(0, 1) [L] and a selection bias b = 0.05 N(0, 1) [E],
+    both float32, for tests that exercise the gain and a bias moved away from zero."""
+    gamma = (1.0 + 0.5 * _normal((cfg.d_latent,), 1.0, seed, TID_GAMMA)).astype(np.float32)
+    bias = (0.05 * _normal((cfg.n_experts,), 1.0, seed, TID_BIAS)).astype(np.float32)
+    return gamma, bias
+
+
+def make_inputs(cfg: LayerConfig, seed: int = 0, batch: int = 0, with_x: bool = True, gain_bias: bool = False) -> dict:
     """All tensors of one layer instance as host arrays (bf16 as uint16 bit patterns)."""
     T, D, L, E, I = cfg.T, cfg.d_model, cfg.d_latent, cfg.n_experts, cfg.inter
     S, Is, dt = cfg.n_shared, cfg.inter_shared, cfg.act_dtype
@@ -130,6 +139,8 @@ def make_inputs(cfg: LayerConfig, seed: int = 0, batch: int = 0, with_x: bool = 
         "w1s": np.stack([_weight((2 * Is, D), D, dt, seed, TID_W1S, j) for j in range(S)]),
         "w2s": np.stack([_weight((D, Is), Is, dt, seed, TID_W2S, j) for j in range(S)]),
     }
+    if gain_bias:
+        out["gamma"], out["bias"] = gain_and_bias(cfg, seed)
     if with_x:
         out["x"] = token_rows(cfg, seed, batch)
     return out
