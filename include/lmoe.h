@@ -163,6 +163,23 @@ lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* shape, int32_t n_groups, int
                                   const void* w2, void* h, void* y, int32_t y_dtype, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* lmoe_grouped_situ_glu without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation). Same arguments
+ * and results, except that:
+ *   - the grouped m-tile list lives in a 16 KiB array of the library's own device memory, one per
+ *     device, held until the process ends: n_groups + 1 <= 4096, else LMOE_ERR_UNSUPPORTED;
+ *   - dense calls (group_offsets NULL) run without split-K partials (same results up to f32
+ *     summation order; slower on small batches).
+ * Every call on one device shares that device's array: calls that overlap on one device (other
+ * streams, other host threads) race and must be ordered by the caller. The array's contents are
+ * rewritten in full by each call, nothing needs clearing. Allocates nothing (no hipMalloc, no
+ * library allocation); the first call on a device looks the array's address up once. */
+lmoe_status lmoe_grouped_situ_glu_noalloc(const lmoe_shape* shape, int32_t n_groups, int32_t rows, int32_t K,
+                                          int32_t inter, int32_t n_out, const void* a, int32_t a_rows,
+                                          const int32_t* a_row_index, const int32_t* group_offsets,
+                                          const void* w1, const void* w2, void* h, void* y, int32_t y_dtype,
+                                          void* stream);
+
 /* Shared experts as one FFN ([vxz] 01: always-on shared experts; by linearity S SiTU-GLU experts
  * equal one of inner size S*I_s with the gate blocks, up blocks and down blocks concatenated).
  * One-time weight repack, not part of the per-batch pass:

@@ -22,12 +22,12 @@ LMOE_CALL_BWD_UP, LMOE_CALL_BWD_COMBINE_NORM, LMOE_CALL_BWD_EXPERTS, LMOE_CALL_B
     16, 17, 18, 19, 20
 
 # every symbol include/lmoe.h declares
-EXPORTS = ("lmoe_workspace_bytes", "lmoe_status_string", "lmoe_split_router", "lmoe_route", "lmoe_qb_histogram", "lmoe_qb_update",
-           "lmoe_permute", "lmoe_grouped_situ_glu", "lmoe_pack_shared", "lmoe_combine_norm_up",
-           "lmoe_bwd_transpose_weights", "lmoe_bwd_up", "lmoe_bwd_combine_norm", "lmoe_bwd_router",
-           "lmoe_bwd_experts", "lmoe_bwd_down", "lmoe_bwd_shared", "lmoe_mx_quantize", "lmoe_grouped_situ_glu_mx",
-           "lmoe_profile_enable", "lmoe_profile_only", "lmoe_profile_reset", "lmoe_profile_collect",
-           "lmoe_profile_get")
+EXPORTS = ("lmoe_workspace_bytes", "lmoe_status_string", "lmoe_split_router", "lmoe_route", "lmoe_qb_histogram",
+           "lmoe_qb_update", "lmoe_permute", "lmoe_grouped_situ_glu", "lmoe_grouped_situ_glu_noalloc",
+           "lmoe_pack_shared", "lmoe_combine_norm_up", "lmoe_bwd_transpose_weights", "lmoe_bwd_up",
+           "lmoe_bwd_combine_norm", "lmoe_bwd_router", "lmoe_bwd_experts", "lmoe_bwd_down", "lmoe_bwd_shared",
+           "lmoe_mx_quantize", "lmoe_grouped_situ_glu_mx", "lmoe_profile_enable", "lmoe_profile_only",
+           "lmoe_profile_reset", "lmoe_profile_collect", "lmoe_profile_get")
 
 
 class LmoeError(RuntimeError):
@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
             "lmoe_grouped_situ_glu": (ctypes.c_int, [_S, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                      ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P,
                                                      _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
+            "lmoe_grouped_situ_glu_noalloc": (ctypes.c_int, [_S, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                             ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P,
+                                                             _P, _P, _P, _P, _P, ctypes.c_int32, _P]),
             "lmoe_pack_shared": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
             "lmoe_combine_norm_up": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                     _P, ctypes.c_size_t, _P]),
@@ -178,6 +181,17 @@ def lmoe_grouped_situ_glu(shape, n_groups: int, rows: int, K: int, inter: int, n
            lib().lmoe_grouped_situ_glu(ctypes.byref(shape), n_groups, rows, K, inter, n_out, _ptr(a), a_rows,
                                        _ptr(a_row_index), _ptr(group_offsets), _ptr(w1), _ptr(w2), _ptr(h), _ptr(y),
                                        y_dtype, _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def lmoe_grouped_situ_glu_noalloc(shape, n_groups: int, rows: int, K: int, inter: int, n_out: int, a, group_offsets,
+                                  w1, w2, h, y, a_row_index=None, stream=None):
+    """lmoe_grouped_situ_glu without a workspace (the library's own per-device scratch array)."""
+    y_dtype = LMOE_F32 if (y is not None and y.dtype == torch.float32) else LMOE_BF16
+    a_rows = a.shape[0] if a_row_index is not None else rows
+    _check("lmoe_grouped_situ_glu_noalloc",
+           lib().lmoe_grouped_situ_glu_noalloc(ctypes.byref(shape), n_groups, rows, K, inter, n_out, _ptr(a), a_rows,
+                                               _ptr(a_row_index), _ptr(group_offsets), _ptr(w1), _ptr(w2), _ptr(h),
+                                               _ptr(y), y_dtype, _stream(stream)))
 
 
 def lmoe_pack_shared(shape, w1s, w2s, w1s_packed, w2s_packed, stream=None):

@@ -1,5 +1,7 @@
 // C ABI of the library: argument validation (before anything is enqueued), workspace sizing and the
 // composition of kernels behind each call.
+#include <mutex>
+
 #include "common.h"
 
 using namespace lmoe;
@@ -261,10 +263,15 @@ lmoe_status lmoe_permute(const lmoe_shape* sh, const void* x, const void* w_down
   return hip_status(launch_gather_rows(x_lat, slot_of_pair, T, k, (int64_t)L * esize(sh->act_dtype), x_perm, s));
 }
 
-lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* sh, int32_t G, int32_t rows, int32_t K, int32_t inter,
-                                  int32_t n_out, const void* a_in, int32_t a_rows, const int32_t* a_row_index,
-                                  const int32_t* group_offsets, const void* w1, const void* w2, void* h, void* y,
-                                  int32_t y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation of lmoe_grouped_situ_glu's arguments other than the workspace.
+lmoe_status check_grouped(const lmoe_shape* sh, int32_t G, int32_t rows, int32_t K, int32_t inter, int32_t n_out,
+                          const void* a_in, int32_t a_rows, const int32_t* a_row_index,
+                          const int32_t* group_offsets, const void* w1, const void* w2, void* h, void* y,
+                          int32_t y_dtype) {
   lmoe_status st = check_shape(sh);
   if (st != LMOE_OK) return st;
   if (G < 1 || rows < 0 || a_rows < 0 || K <= 0 || inter <= 0 || (w2 && n_out <= 0)) return LMOE_ERR_INVALID_ARGUMENT;
@@ -278,20 +285,26 @@ lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* sh, int32_t G, int32_t rows,
   if (!aligned16(a_in) || !aligned16(w1) || !aligned16(h) || (a_row_index && !aligned4(a_row_index)) ||
       (group_offsets && !aligned4(group_offsets)) || (w2 && (!aligned16(w2) || !aligned16(y))))
     return LMOE_ERR_INVALID_ARGUMENT;
-  const size_t need = group_offsets ? glu_ws(G) : 0;
-  if (need && (!workspace || workspace_bytes < need || !aligned16(workspace))) return LMOE_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int dt = sh->act_dtype;
+  return LMOE_OK;
+}
 
+// The grouped GEMMs with the m-tile list in `mts` (G + 1 ints, grouped calls only) and optional
+// split-K partials (dense calls: `split_ws`, nullptr = run unsplit).
+lmoe_status grouped_glu(const lmoe_shape* sh, int32_t G, int32_t rows, int32_t K, int32_t inter, int32_t n_out,
+                        const void* a_in, int32_t a_rows, const int32_t* a_row_index, const int32_t* group_offsets,
+                        const void* w1, const void* w2, void* h, void* y, int32_t y_dtype, int32_t* mts_buf,
+                        void* split_ws, size_t split_ws_bytes, hipStream_t s) {
+  lmoe_status st = LMOE_OK;
+  const int dt = sh->act_dtype;
   GemmShape shape;
   if (group_offsets) {
     shape = (int64_t)rows >= (int64_t)G * 64 ? GemmShape::Big : GemmShape::Small;
-    st = hip_status(launch_mtile_prefix(group_offsets, G, gemm_block_m(shape), static_cast<int32_t*>(workspace), s));
+    st = hip_status(launch_mtile_prefix(group_offsets, G, gemm_block_m(shape), mts_buf, s));
     if (st != LMOE_OK) return st;
   } else {
     shape = dense_shape(rows, ceil_div(inter, 128));
   }
-  const int32_t* mts = group_offsets ? static_cast<const int32_t*>(workspace) : nullptr;
+  const int32_t* mts = group_offsets ? mts_buf : nullptr;
 
   GemmArgs g1 = gemm_args();
   g1.A = a_in;
@@ -315,15 +328,14 @@ lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* sh, int32_t G, int32_t rows,
   g1.beta1 = sh->beta1;
   g1.beta2 = sh->beta2;
   g1.tag = group_offsets ? "gemm_glu_grouped" : "gemm_glu_dense";
-  const size_t base = round_up(need);
   SplitPlan sp1, sp2;
   float *part1 = nullptr, *part2 = nullptr;
-  if (!group_offsets && !a_row_index) {
+  if (!group_offsets && !a_row_index && split_ws) {
     sp1 = plan_split_k(rows, 2 * (int64_t)inter, K, 0, K, esize(dt));
-    part1 = split_region(sp1, rows, 2 * (int64_t)inter, workspace, workspace_bytes, base);
+    part1 = split_region(sp1, rows, 2 * (int64_t)inter, split_ws, split_ws_bytes, 0);
     if (w2) {
       sp2 = plan_split_k(rows, n_out, inter, 0, inter, esize(dt));
-      part2 = split_region(sp2, rows, n_out, workspace, workspace_bytes, base);
+      part2 = split_region(sp2, rows, n_out, split_ws, split_ws_bytes, 0);
     }
   }
   st = hip_status(run_gemm(g1, dt, Epi::Glu, shape, sp1, part1, s));
@@ -347,6 +359,71 @@ lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* sh, int32_t G, int32_t rows,
   if (!group_offsets) shape = dense_shape(rows, ceil_div(n_out, 256));
   return hip_status(run_gemm(g2, dt, Epi::Store, shape, sp2, part2, s));
 }
+
+// Scratch of lmoe_grouped_situ_glu_noalloc: the m-tile list (G + 1 ints), on every device.
+constexpr size_t kNoAllocScratchBytes = 16384;
+__device__ __align__(256) int32_t scratch[kNoAllocScratchBytes / sizeof(int32_t)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up once per device.
+lmoe_status noalloc_scratch(int32_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LMOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return LMOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LMOE_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return LMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lmoe_status lmoe_grouped_situ_glu(const lmoe_shape* sh, int32_t G, int32_t rows, int32_t K, int32_t inter,
+                                  int32_t n_out, const void* a_in, int32_t a_rows, const int32_t* a_row_index,
+                                  const int32_t* group_offsets, const void* w1, const void* w2, void* h, void* y,
+                                  int32_t y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  lmoe_status st = check_grouped(sh, G, rows, K, inter, n_out, a_in, a_rows, a_row_index, group_offsets, w1, w2, h, y,
+                                 y_dtype);
+  if (st != LMOE_OK || rows == 0) return st;
+  const size_t need = group_offsets ? glu_ws(G) : 0;
+  if (need && (!workspace || workspace_bytes < need || !aligned16(workspace))) return LMOE_ERR_WORKSPACE;
+  const size_t base = round_up(need);
+  void* split_ws = workspace && aligned16(workspace) && workspace_bytes > base ? static_cast<char*>(workspace) + base
+                                                                               : nullptr;
+  return grouped_glu(sh, G, rows, K, inter, n_out, a_in, a_rows, a_row_index, group_offsets, w1, w2, h, y, y_dtype,
+                     static_cast<int32_t*>(workspace), split_ws, split_ws ? workspace_bytes - base : 0,
+                     static_cast<hipStream_t>(stream));
+}
+
+lmoe_status lmoe_grouped_situ_glu_noalloc(const lmoe_shape* sh, int32_t G, int32_t rows, int32_t K, int32_t inter,
+                                          int32_t n_out, const void* a_in, int32_t a_rows,
+                                          const int32_t* a_row_index, const int32_t* group_offsets, const void* w1,
+                                          const void* w2, void* h, void* y, int32_t y_dtype, void* stream) {
+  lmoe_status st = check_grouped(sh, G, rows, K, inter, n_out, a_in, a_rows, a_row_index, group_offsets, w1, w2, h, y,
+                                 y_dtype);
+  if (st != LMOE_OK || rows == 0) return st;
+  if ((size_t)(G + 1) * sizeof(int32_t) > kNoAllocScratchBytes) return LMOE_ERR_UNSUPPORTED;
+  int32_t* mts = nullptr;
+  if (group_offsets) {
+    st = noalloc_scratch(&mts);
+    if (st != LMOE_OK) return st;
+  }
+  return grouped_glu(sh, G, rows, K, inter, n_out, a_in, a_rows, a_row_index, group_offsets, w1, w2, h, y, y_dtype,
+                     mts, nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+extern "C" {
 
 lmoe_status lmoe_pack_shared(const lmoe_shape* sh, const void* w1s, const void* w2s, void* w1s_packed,
                              void* w2s_packed, void* stream) {
