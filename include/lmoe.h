@@ -124,11 +124,14 @@ lmoe_status lmoe_qb_update(const lmoe_shape* shape, uint32_t* hist, int64_t n_ac
  * [slm] 训练基础设施: static shapes, no host synchronisation).
  *   x              [T, D] act_dtype
  *   w_down         [L, D] act_dtype
- *   topk_idx       [T, k] i32
+ *   topk_idx       [T, k] i32               expert ids; an id outside [0, E), or one a row lists a
+ *                                           second time, drops that pair (slot -1, no sorted row)
  *   x_lat          [T, L] act_dtype (out)   x . w_down^T
- *   expert_offsets [E + 1] i32 (out)        first sorted row of each expert; [E] = T*k
+ *   expert_offsets [E + 1] i32 (out)        first sorted row of each expert; [E] = pairs kept (T*k
+ *                                           when every row holds k distinct ids in [0, E), as
+ *                                           lmoe_route writes them)
  *   sorted_token   [T*k] i32 (out)          token of each sorted row (tokens ascending per expert)
- *   slot_of_pair   [T*k] i32 (out)          sorted row of pair t*k + j
+ *   slot_of_pair   [T*k] i32 (out)          sorted row of pair t*k + j (-1 for a dropped pair)
  *   x_perm         [T*k, L] act_dtype (out) x_lat[sorted_token[r]], or NULL to skip the copy (the
  *                                           routed GEMM can read x_lat through sorted_token)
  *   workspace      LMOE_CALL_PERMUTE bytes                                                         */

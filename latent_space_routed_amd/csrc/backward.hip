@@ -191,6 +191,7 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(const T* __restrict__ 
       for (int v = 0; v < V; ++v) z[i][v] = 0.0f;
     for (int j = 0; j < k; ++j) {
       const int32_t slot = slot_of_pair[t * k + j];
+      if (slot < 0) continue;  // a pair the permutation dropped
       const float wj = topk_w[t * k + j];
       const T* row = y + (int64_t)slot * L;
 #pragma unroll
@@ -254,7 +255,7 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(const T* __restrict__ 
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const int c = lane + 64 * i;
-        if (c < chunks) {
+        if (c < chunks && slot >= 0) {
           float f[V], o[V];
           Vec<T>::unpack(*reinterpret_cast<const uint4*>(row + (int64_t)c * V), f);
 #pragma unroll
@@ -266,7 +267,7 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(const T* __restrict__ 
         }
       }
       dot = wave_sum(dot);
-      if (lane == j) {
+      if (lane == j && slot >= 0) {
         my_dw = dot;
         my_w = wj;
         my_slot = slot;
@@ -279,7 +280,7 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(const T* __restrict__ 
       const float ds = (my_dw - wdw) / S;
       const float g = ds * my_s * (1.0f - my_s);
       dl[t * k + lane] = g;
-      dl_sorted[my_slot] = g;
+      if (my_slot >= 0) dl_sorted[my_slot] = g;
     }
   }
   // dgamma: block partial = wave 0 + wave 1 + wave 2 + wave 3, in that order
@@ -386,7 +387,9 @@ __global__ void __launch_bounds__(256) unpermute_kernel(const T* __restrict__ sr
 #pragma unroll
     for (int v = 0; v < V; ++v) a[i][v] = 0.0f;
   for (int j = 0; j < k; ++j) {
-    const T* row = src + (int64_t)slot_of_pair[t * k + j] * L;
+    const int32_t slot = slot_of_pair[t * k + j];
+    if (slot < 0) continue;  // a pair the permutation dropped
+    const T* row = src + (int64_t)slot * L;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = lane + 64 * i;

@@ -2,12 +2,16 @@
 // device (no host synchronisation, static shapes: [slm] 训练基础设施), then a gather of latent rows.
 //
 //   count   : per 256-token chunk, how many of its tokens chose each expert      -> cc[chunk][e]
+//             (every wave marks its 64 tokens' experts in an LDS bitmask per expert; the count is
+//             the masks' popcount, so a token that lists an expert twice counts once)
 //   scan    : exclusive prefix over chunks (in place) and over experts          -> offsets[E+1]
 //   scatter : per chunk, every wave marks its 64 tokens' experts in an LDS bitmask per expert; the
 //             rank of token t inside expert e is offsets[e] + cc[chunk][e] + (tokens of earlier
 //             waves) + popcount(mask_e & lanes below t). Tokens therefore ascend inside an expert.
 //   gather  : one wave per token loads its latent row once and writes it to its k sorted rows.
-// An expert index outside [0, E) drops the pair: its slot is -1 and later kernels skip it.
+// An expert index outside [0, E), or one that a token lists a second time, drops the pair: its slot is
+// -1, it takes no sorted row, and later kernels skip it. expert_offsets[E] is then the number of
+// pairs kept.
 #include <mutex>
 
 #include "common.h"
@@ -19,18 +23,25 @@ constexpr int kMaxExpertsLds = 2048;  // the library's largest expert count
 
 __global__ void __launch_bounds__(kPermChunk) perm_count_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
                                                                  int32_t* __restrict__ cc) {
-  extern __shared__ int32_t cnt[];  // [E]
-  for (int e = threadIdx.x; e < E; e += kPermChunk) cnt[e] = 0;
+  extern __shared__ unsigned long long marks[];  // [4][E]: bit l of marks[w][e] = token 64 w + l chose e
+  constexpr int W = kPermChunk / 64;
+  for (int i = threadIdx.x; i < W * E; i += kPermChunk) marks[i] = 0ull;
   __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * kPermChunk + threadIdx.x;
   if (t < T) {
     for (int j = 0; j < k; ++j) {
       const int e = idx[t * k + j];
-      if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+      if (e >= 0 && e < E) atomicOr(&marks[wave * E + e], 1ull << lane);
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kPermChunk) cc[(int64_t)blockIdx.x * E + e] = cnt[e];
+  for (int e = threadIdx.x; e < E; e += kPermChunk) {
+    int n = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) n += __popcll(marks[w * E + e]);
+    cc[(int64_t)blockIdx.x * E + e] = n;
+  }
 }
 
 __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ cc, int chunks, int E,
@@ -94,15 +105,19 @@ __global__ void __launch_bounds__(kPermChunk) perm_scatter_kernel(const int32_t*
   const int64_t t = (int64_t)blockIdx.x * kPermChunk + threadIdx.x;
   const bool live = t < T;
   // The token's pairs are handled KB at a time: their expert indices, then the expert bases, are
-  // loaded together, so a pair's loads do not wait on the previous pair's stores.
+  // loaded together, so a pair's loads do not wait on the previous pair's stores. The pairs of a
+  // token set their bits in order, so a pair whose bit is already set repeats an earlier pair's
+  // expert (bit j of `rep`) and is dropped.
   constexpr int KB = 8;
+  unsigned long long rep = 0ull;
   for (int j0 = 0; j0 < k; j0 += KB) {
     int e[KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) e[i] = (live && j0 + i < k) ? idx[t * k + j0 + i] : -1;
 #pragma unroll
     for (int i = 0; i < KB; ++i)
-      if (e[i] >= 0 && e[i] < E) atomicOr(&bits[wave * E + e[i]], 1ull << lane);
+      if (e[i] >= 0 && e[i] < E && (atomicOr(&bits[wave * E + e[i]], 1ull << lane) >> lane & 1ull))
+        rep |= 1ull << (j0 + i);
   }
   __syncthreads();
   if (!live) return;
@@ -112,7 +127,7 @@ __global__ void __launch_bounds__(kPermChunk) perm_scatter_kernel(const int32_t*
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
       e[i] = j0 + i < k ? idx[t * k + j0 + i] : -1;
-      if (e[i] >= E) e[i] = -1;
+      if (e[i] >= E || (rep >> ((j0 + i) & 63) & 1ull)) e[i] = -1;
     }
 #pragma unroll
     for (int i = 0; i < KB; ++i) base[i] = e[i] >= 0 ? base_e[e[i]] : 0;
@@ -190,7 +205,15 @@ hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* offs
   const int chunks = (int)ceil_div(T, kPermChunk);
   {
     KernelTimer timer("perm_count", s);
-    hipLaunchKernelGGL(perm_count_kernel, dim3(chunks), dim3(kPermChunk), (size_t)E * 4, s, idx, T, E, k, cc);
+    static std::once_flag once;  // the masks pass the default 64 KB of dynamic LDS at the largest expert counts
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+      attr = hipFuncSetAttribute((const void*)perm_count_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 kMaxExpertsLds * 8 * (kPermChunk / 64));
+    });
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(perm_count_kernel, dim3(chunks), dim3(kPermChunk), (size_t)E * 8 * (kPermChunk / 64), s, idx,
+                       T, E, k, cc);
   }
   {
     KernelTimer timer("perm_scan", s);

@@ -178,3 +178,50 @@ def test_permute_large_expert_counts(E):
     np.testing.assert_array_equal(off.cpu().numpy(), ref_off)
     np.testing.assert_array_equal(st.cpu().numpy(), ref_st)
     np.testing.assert_array_equal(sp.cpu().numpy(), ref_sp)
+
+
+def test_permute_drops_repeated_and_out_of_range_ids():
+    """Rows that list an expert twice, or ids outside [0, E): each such pair is dropped (slot -1,
+    no sorted row), the first occurrence of an expert in a row is kept, and the kept pairs are
+    sorted exactly as a stable sort by expert of the kept (token, slot) pairs."""
+    T, D, k, E = 600, 128, 8, 40
+    cfg = replace(CONFIGS["mid_bf16"], T=T, d_model=D, n_experts=E, top_k=k)
+    rng = np.random.default_rng(5)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)       # many rows repeat an expert
+    idx[::7, 3] = E + 5                                          # out of range
+    idx[::11, 0] = -2
+    idx[::13, 1:] = idx[::13, :1]                                # a row of one expert k times
+    # expected: keep the first occurrence of each in-range expert in a row, stable sort by expert
+    keep = np.zeros((T, k), bool)
+    for t in range(T):
+        seen = set()
+        for j in range(k):
+            e = int(idx[t, j])
+            if 0 <= e < E and e not in seen:
+                keep[t, j] = True
+                seen.add(e)
+    pairs = [(int(idx[t, j]), t, j) for t in range(T) for j in range(k) if keep[t, j]]
+    pairs.sort(key=lambda p: (p[0], p[1]))                       # by expert, tokens ascending
+    ref_sp = np.full(T * k, -1, np.int32)
+    ref_st = np.empty(len(pairs), np.int32)
+    for r, (e, t, j) in enumerate(pairs):
+        ref_sp[t * k + j] = r
+        ref_st[r] = t
+    counts = np.bincount([p[0] for p in pairs], minlength=E)
+    ref_off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    dev = "cuda"
+    shape = C.make_shape(cfg, T)
+    x = torch.randn(T, D, device=dev).to(torch.bfloat16)
+    w_down = (torch.randn(cfg.d_latent, D, device=dev) * D ** -0.5).to(torch.bfloat16)
+    x_lat = torch.empty(T, cfg.d_latent, dtype=torch.bfloat16, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    st = torch.full((T * k,), -7, dtype=torch.int32, device=dev)
+    sp = torch.empty(T * k, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(C.workspace_bytes(shape, C.LMOE_CALL_PERMUTE), 256), dtype=torch.uint8, device=dev)
+    C.lmoe_permute(shape, x, w_down, torch.as_tensor(idx).to(dev), x_lat, off, st, sp, None, ws)
+    torch.cuda.synchronize()
+    say(f"permute with dropped pairs: kept {len(pairs)} of {T * k}")
+    np.testing.assert_array_equal(off.cpu().numpy(), ref_off)
+    np.testing.assert_array_equal(sp.cpu().numpy(), ref_sp)
+    np.testing.assert_array_equal(st.cpu().numpy()[: len(pairs)], ref_st)
+    assert (st.cpu().numpy()[len(pairs):] == -7).all()           # no sorted row beyond the kept pairs
