@@ -43,6 +43,14 @@ struct Vec<float> {
   }
 };
 
+// 16-byte load with the non-temporal hint: every y row is read once, here, so it is streamed past
+// the caches (measured at K3 prefill: 0.219 -> 0.196 ms).
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ inline uint4 load16_nt(const void* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <typename T, int CPL>
 __global__ void __launch_bounds__(256) combine_norm_kernel(const T* __restrict__ y, const int32_t* __restrict__ slot_of_pair,
                                                            const float* __restrict__ w, const float* __restrict__ gamma,
@@ -73,10 +81,8 @@ __global__ void __launch_bounds__(256) combine_norm_kernel(const T* __restrict__
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = lane + 64 * i;
-      r0[i] = (c < chunks && s0 >= 0) ? *reinterpret_cast<const uint4*>(y + (int64_t)s0 * L + (int64_t)c * V)
-                                      : make_uint4(0, 0, 0, 0);
-      r1[i] = (c < chunks && s1 >= 0) ? *reinterpret_cast<const uint4*>(y + (int64_t)s1 * L + (int64_t)c * V)
-                                      : make_uint4(0, 0, 0, 0);
+      r0[i] = (c < chunks && s0 >= 0) ? load16_nt(y + (int64_t)s0 * L + (int64_t)c * V) : make_uint4(0, 0, 0, 0);
+      r1[i] = (c < chunks && s1 >= 0) ? load16_nt(y + (int64_t)s1 * L + (int64_t)c * V) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {

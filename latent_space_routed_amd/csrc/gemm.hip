@@ -244,7 +244,7 @@ __device__ inline void epilogue(const GemmArgs& p, const TileInfo& t, f32x16 (&a
 // LDS region in row-major order, then every lane stores whole 16-byte chunks (one instruction per
 // 8 bf16 or 4 f32) instead of one scalar per element. Needs N and ldc multiples of 16 / sizeof(TO)
 // and a 16-byte aligned C. Row-blocks are staged RBP at a time to fit the region.
-template <typename TI, typename TO, int WAVES_M, int WAVES_N, int WM, int WN, Epi EPI, int REGION>
+template <typename TI, typename TO, int WAVES_M, int WAVES_N, int WM, int WN, Epi EPI, int REGION, bool NTC = false>
 __device__ inline void epilogue_staged(const GemmArgs& p, const TileInfo& t, f32x16 (&acc)[WM][WN], int wm, int wn,
                                        int lane, int na, char* region) {
   constexpr bool GLU = EPI == Epi::Glu;
@@ -286,9 +286,15 @@ __device__ inline void epilogue_staged(const GemmArgs& p, const TileInfo& t, f32
       const int j = cc / CPB, cv = (cc % CPB) * VEC;
       const int r = ((i0 + lr / 32) * WAVES_M + wm) * 32 + (lr % 32);
       const int col = t.n0 + (j * WAVES_N + wn) * 32 + cv;
-      if (r < t.rows && col < p.N)
-        *reinterpret_cast<uint4*>(static_cast<TO*>(p.C) + (int64_t)(t.row0 + r) * p.ldc + col + t.coff) =
-            *reinterpret_cast<const uint4*>(region + lr * ROWB + (j * 32 + cv) * (int)sizeof(TO));
+      if (r < t.rows && col < p.N) {
+        uint4* dst = reinterpret_cast<uint4*>(static_cast<TO*>(p.C) + (int64_t)(t.row0 + r) * p.ldc + col + t.coff);
+        const uint4 v = *reinterpret_cast<const uint4*>(region + lr * ROWB + (j * 32 + cv) * (int)sizeof(TO));
+        if constexpr (NTC) {
+          __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
+        } else {
+          *dst = v;
+        }
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -324,10 +330,12 @@ __device__ inline void dispatch_na(int na, F&& f) {
 // LDS with the 16-byte chunk c of row k at slot c ^ (k % 16); a B fragment (8 consecutive k of one
 // column) is gathered with 16-bit LDS reads, which the swizzle spreads over distinct banks.
 // NTB: B is streamed through once (the routed experts' W1): its DMA carries the non-temporal hint.
+// NTC: C is written once and read once later (the routed experts' y): stored with the non-temporal
+// hint (measured at K3 prefill: the combine that reads y 0.196 -> 0.189 ms, GEMM2 unchanged).
 // XB: B's ring holds XB more stages than A's, and B's K-tiles are issued XB tiles further ahead
 // (two A stages and three B stages of 64-element K-tiles fill the 160 KB of LDS).
 template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, int NS, int KB, Epi EPI, bool BKN = false,
-          bool NTB = false, int XB = 0>
+          bool NTB = false, int XB = 0, bool NTC = false>
 __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
     __attribute__((amdgpu_waves_per_eu(WAVES_M* WAVES_N / 4, WAVES_M* WAVES_N / 4)))  // one workgroup per CU
     gemm_dma_kernel(GemmArgs p_in) {
@@ -554,9 +562,10 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
       __syncthreads();  // every wave is done reading the pipeline stages
       char* region = smem + wave * REGION;
       if (bf)
-        epilogue_staged<TI, uint16_t, WAVES_M, WAVES_N, WM, WN, EPI, REGION>(p, t, acc, wm, wn, lane, na, region);
+        epilogue_staged<TI, uint16_t, WAVES_M, WAVES_N, WM, WN, EPI, REGION, NTC>(p, t, acc, wm, wn, lane, na,
+                                                                                 region);
       else
-        epilogue_staged<TI, float, WAVES_M, WAVES_N, WM, WN, EPI, REGION>(p, t, acc, wm, wn, lane, na, region);
+        epilogue_staged<TI, float, WAVES_M, WAVES_N, WM, WN, EPI, REGION, NTC>(p, t, acc, wm, wn, lane, na, region);
       return;
     }
   }
@@ -1095,9 +1104,9 @@ hipError_t launch_big(const GemmArgs& a, Epi epi, hipStream_t s) {
                        block, 0, s, a);
     return hipGetLastError();
   }
-  if (epi == Epi::Store && a.goff && !a.koff && !a.A2 && a.splits <= 1) {  // routed GEMM2: W2 streamed, non-temporal
-    hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Store, false, true, 1>), grid,
-                       block, 0, s, a);
+  if (epi == Epi::Store && a.goff && !a.koff && !a.A2 && a.splits <= 1) {  // routed GEMM2: W2 in, y out, non-temporal
+    hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Store, false, true, 1, true>),
+                       grid, block, 0, s, a);
     return hipGetLastError();
   }
   LMOE_LAUNCH_EPI(gemm_dma_kernel, TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes)
