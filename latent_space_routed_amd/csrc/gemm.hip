@@ -142,16 +142,18 @@ struct TileInfo {
   int64_t coff;   // element offset of the tile's output block (K-grouped GEMMs)
 };
 
+// Tile of (virtual) workgroup vb: workgroup vb runs on XCD vb % 8, and each XCD takes a contiguous
+// run of tile numbers, so that the n-tiles of one m-tile share that XCD's L2.
 template <int BM, int BNO>
-__device__ inline bool assign_tile(const GemmArgs& p, TileInfo& t) {
+__device__ inline bool assign_tile(const GemmArgs& p, TileInfo& t, int vb) {
   const bool grouped = p.goff != nullptr;
   const int n_tiles = (int)ceil_div(p.N, BNO);
   const int mt_total = p.koff ? p.G * (int)ceil_div(p.M, BM) : grouped ? p.mtile_start[p.G] : (int)ceil_div(p.M, BM);
   const int total = mt_total * n_tiles;
   const int per = (total + kXcds - 1) / kXcds;
-  const int loc = blockIdx.x / kXcds;
+  const int loc = vb / kXcds;
   if (loc >= per) return false;
-  const int lt = (blockIdx.x % kXcds) * per + loc;
+  const int lt = (vb % kXcds) * per + loc;
   if (lt >= total) return false;
   int n_tile;
   t.g = 0;
@@ -323,6 +325,52 @@ __device__ inline void dispatch_na(int na, F&& f) {
   }
 }
 
+// MFMAs of one K-tile of the DMA pipeline: A's stage at `base` (BM rows of KB bytes), B's at `bbase`
+// (BNB rows of KB bytes, or KB/sizeof(TI) k-rows of BNB columns when BKN), both swizzled by swz<KB>.
+// The fragments of k-step s + 1 are read from LDS while the MFMAs of k-step s run.
+template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, int KB, bool GLU, bool BKN, int NA>
+__device__ inline void dma_ktile(const char* base, const char* bbase, const int (&fo)[KB / 32], int wm, int wn,
+                                 int lane, f32x16 (&acc)[WM][WN]) {
+  constexpr int KS = KB / 32;
+  constexpr int BNB = WAVES_N * WN * 32;
+  constexpr int BNO = GLU ? BNB / 2 : BNB;
+  constexpr int WNO = GLU ? WN / 2 : WN;
+  constexpr int BROW = BNB * (int)sizeof(TI);  // bytes of one k-row of a [K, N] B tile
+  uint4 af[2][NA > 0 ? NA : 1], bf[2][WN];
+  auto load = [&](int s, uint4 (&a)[NA > 0 ? NA : 1], uint4 (&b)[WN]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      a[i] = *reinterpret_cast<const uint4*>(base + (i * WAVES_M + wm) * 32 * KB + fo[s]);
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int ocb = (j % WNO) * WAVES_N + wn;
+      const int bblk = (GLU && j >= WNO) ? BNO / 32 + ocb : ocb;
+      if constexpr (BKN) {
+        const int n = bblk * 32 + (lane & 31), c = n >> 3, e = n & 7;
+        const int k0 = s * 16 + 8 * (lane >> 5);
+        uint16_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          v[i] = *reinterpret_cast<const uint16_t*>(bbase + (k0 + i) * BROW + ((c ^ ((k0 + i) & 15)) << 4) + e * 2);
+        b[j] = *reinterpret_cast<const uint4*>(v);
+      } else {
+        b[j] = *reinterpret_cast<const uint4*>(bbase + bblk * 32 * KB + fo[s]);
+      }
+    }
+  };
+  load(0, af[0], bf[0]);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (s + 1 < KS) load(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) Mfma<TI>::run(acc[i][j], af[s & 1][i], bf[s & 1][j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ------------------------------------------------------------------------------------------------
 // DMA pipeline: 256x256 tiles, LDS fed straight from HBM, three K-tiles in flight
 // ------------------------------------------------------------------------------------------------
@@ -371,7 +419,7 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   TileInfo t;
-  if (!assign_tile<BM, BNO>(p, t)) return;
+  if (!assign_tile<BM, BNO>(p, t, blockIdx.x)) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -388,7 +436,6 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
                               : make_desc(static_cast<const char*>(p.A) + (int64_t)t.row0 * a_ld +
                                               (int64_t)t.k0 * (int64_t)sizeof(TI), (int)(t.rows * a_ld));
   static_assert(!BKN || (sizeof(TI) == 2 && KB == 128 && !GLU && EPI == Epi::Store), "[K, N] B: bf16 store");
-  constexpr int BROW = BNB * (int)sizeof(TI);  // bytes of one k-row of a [K, N] B tile
   const u32x4 b_desc0 = BKN ? make_desc(Bb + (int64_t)t.n0 * (int64_t)sizeof(TI),
                                         (int)((int64_t)p.K * b_ld - (int64_t)t.n0 * (int64_t)sizeof(TI)))
                             : make_desc(Bb + (int64_t)t.n0 * b_ld, (int)(ncols * b_ld));
@@ -485,43 +532,8 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
   dispatch_na<WM>(na, [&](auto na_c) __attribute__((always_inline)) {
     constexpr int NA = decltype(na_c)::value;
     auto compute = [&](int sa, int sb) __attribute__((always_inline)) {
-      const char* base = smem + sa * A_BYTES;
-      const char* bbase = smem + B_BASE + sb * B_BYTES;
-      // fragments of k-step s + 1 are read from LDS while the MFMAs of k-step s run
-      uint4 af[2][NA > 0 ? NA : 1], bf[2][WN];
-      auto load = [&](int s, uint4 (&a)[NA > 0 ? NA : 1], uint4 (&b)[WN]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < NA; ++i)
-          a[i] = *reinterpret_cast<const uint4*>(base + (i * WAVES_M + wm) * 32 * KB + fo[s]);
-#pragma unroll
-        for (int j = 0; j < WN; ++j) {
-          const int ocb = (j % WNO) * WAVES_N + wn;
-          const int bblk = (GLU && j >= WNO) ? BNO / 32 + ocb : ocb;
-          if constexpr (BKN) {
-            const int n = bblk * 32 + (lane & 31), c = n >> 3, e = n & 7;
-            const int k0 = s * 16 + 8 * (lane >> 5);
-            uint16_t v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-              v[i] = *reinterpret_cast<const uint16_t*>(bbase + (k0 + i) * BROW + ((c ^ ((k0 + i) & 15)) << 4) +
-                                                        e * 2);
-            b[j] = *reinterpret_cast<const uint4*>(v);
-          } else {
-            b[j] = *reinterpret_cast<const uint4*>(bbase + bblk * 32 * KB + fo[s]);
-          }
-        }
-      };
-      load(0, af[0], bf[0]);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (s + 1 < KS) load(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < NA; ++i)
-#pragma unroll
-          for (int j = 0; j < WN; ++j) Mfma<TI>::run(acc[i][j], af[s & 1][i], bf[s & 1][j]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      dma_ktile<TI, WAVES_M, WAVES_N, WM, WN, KB, GLU, BKN, NA>(smem + sa * A_BYTES, smem + B_BASE + sb * B_BYTES, fo,
+                                                              wm, wn, lane, acc);
     };
     if constexpr (XB == 0) {
       const int pre = min(KT, NS - 1);
@@ -570,6 +582,162 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
     }
   }
   epilogue<TI, WAVES_M, WAVES_N, WM, WN, EPI>(p, t, acc, wm, wn, lane, na);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Persistent DMA pipeline for the routed experts' GEMMs
+// ------------------------------------------------------------------------------------------------
+// The grouped GEMMs of the routed experts (GEMM1 with the SiTU-GLU epilogue, GEMM2 with a plain
+// store) stream each expert's weights (B) from HBM once. With one workgroup per tile, every tile
+// pays its set-up (tile lookup, row indices), the first DMA round trip and its epilogue with no B
+// bytes in flight: measured at K3 prefill, 11 % of GEMM1's and 42 % of GEMM2's cycles. Here one
+// workgroup per CU walks its XCD's share of the tile numbers (the same numbering as the one-shot
+// launch), and the next tile's first two B K-tiles are in flight while the current tile's epilogue
+// runs. The epilogue is staged through the two A stages only (8 KB per wave), so the B stages can
+// take the next tile's data; the next tile's lookup and row indices are read while the current
+// tile's first K-tile is in flight. Same 256x256 tiles, swizzle, two A and three B stages as the
+// one-shot kernel (B one K-tile further ahead, with the non-temporal hint).
+template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, int KB, Epi EPI, bool NTC>
+__global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
+    __attribute__((amdgpu_waves_per_eu(WAVES_M* WAVES_N / 4, WAVES_M* WAVES_N / 4)))  // one workgroup per CU
+    gemm_routed_kernel(GemmArgs p) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int BM = WAVES_M * WM * 32;
+  constexpr int BNB = WAVES_N * WN * 32;
+  constexpr bool GLU = EPI == Epi::Glu;
+  static_assert(GLU || EPI == Epi::Store, "routed GEMM1 (GLU) or GEMM2 (plain store)");
+  static_assert(!GLU || WN % 2 == 0, "GLU needs gate/up column-block pairs");
+  constexpr int BNO = GLU ? BNB / 2 : BNB;
+  constexpr int RPD = 1024 / KB;
+  constexpr int A_PW = BM / RPD / NW;
+  constexpr int B_PW = BNB / RPD / NW;
+  static_assert(A_PW * RPD * NW == BM && B_PW * RPD * NW == BNB, "DMA split");
+  static_assert(!GLU || BNO % RPD == 0, "a DMA block stays in one GLU half");
+  constexpr int A_BYTES = BM * KB;
+  constexpr int B_BYTES = BNB * KB;
+  constexpr int B_BASE = 2 * A_BYTES;
+  constexpr int LDS_BYTES = B_BASE + 3 * B_BYTES;
+  constexpr int REGION = B_BASE / NW;  // epilogue staging: each wave's slice of the A stages
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+
+  int vb = blockIdx.x;
+  TileInfo t;
+  if (!assign_tile<BM, BNO>(p, t, vb)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int64_t a_ld = p.lda * (int64_t)sizeof(TI), b_ld = p.ldb * (int64_t)sizeof(TI);
+  const bool gather = p.a_rows != nullptr;
+  const int KT = p.K * (int)sizeof(TI) / KB;
+  const int lr = lane / (KB / 16), slot = lane % (KB / 16);
+  const unsigned lds0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
+
+  // Source row of each of the lane's A DMA blocks (gather: the row of A, -1 past the tile's rows).
+  auto load_src = [&](const TileInfo& tt, int (&src)[A_PW]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) {
+      const int r = (wave * A_PW + i) * RPD + lr;
+      src[i] = gather ? (r < tt.rows ? p.a_rows[tt.row0 + r] : -1) : r;
+    }
+  };
+  u32x4 a_desc, b_desc0, b_desc1;
+  int a_voff[A_PW], b_voff[B_PW];
+#pragma unroll
+  for (int i = 0; i < B_PW; ++i) {
+    const int r = (wave * B_PW + i) * RPD + lr;
+    b_voff[i] = (r % BNO) * (int)b_ld + ((slot ^ swz<KB>(r)) * 16);
+  }
+  auto set_a = [&](const TileInfo& tt, const int (&src)[A_PW]) __attribute__((always_inline)) {
+    a_desc = gather ? make_desc(p.A, (int)(p.a_nrows * a_ld))
+                    : make_desc(static_cast<const char*>(p.A) + (int64_t)tt.row0 * a_ld, (int)(tt.rows * a_ld));
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) {
+      const int r = (wave * A_PW + i) * RPD + lr;
+      const int ch = (slot ^ swz<KB>(r)) * 16;
+      if (gather)
+        a_voff[i] = (src[i] >= 0 && src[i] < p.a_nrows) ? src[i] * (int)a_ld + ch : kOutOfRange;
+      else
+        a_voff[i] = r * (int)a_ld + ch;
+    }
+  };
+  auto set_b = [&](const TileInfo& tt) __attribute__((always_inline)) {
+    const char* Bb = static_cast<const char*>(p.B) + (int64_t)tt.g * p.b_gstride * (int64_t)sizeof(TI);
+    const int ncols = min(BNO, p.N - tt.n0);
+    b_desc0 = make_desc(Bb + (int64_t)tt.n0 * b_ld, (int)(ncols * b_ld));
+    b_desc1 = GLU ? make_desc(Bb + (int64_t)(p.glu_up_off + tt.n0) * b_ld, (int)(ncols * b_ld)) : b_desc0;
+  };
+  auto issue_a = [&](int kt, int stage) __attribute__((always_inline)) {
+    const unsigned base = lds0 + stage * A_BYTES;
+#pragma unroll
+    for (int i = 0; i < A_PW; ++i) dma16(a_desc, a_voff[i], kt * KB, base + (wave * A_PW + i) * 1024);
+  };
+  auto issue_b = [&](int kt, int stage) __attribute__((always_inline)) {
+    const unsigned base = lds0 + B_BASE + stage * B_BYTES;
+#pragma unroll
+    for (int i = 0; i < B_PW; ++i) {
+      const bool up = GLU && (wave * B_PW + i) * RPD >= BNO;
+      dma16_nt(up ? b_desc1 : b_desc0, b_voff[i], kt * KB, base + (wave * B_PW + i) * 1024);
+    }
+  };
+  constexpr int KS = KB / 32;
+  int fo[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) fo[s] = (lane & 31) * KB + (((2 * s + (lane >> 5)) ^ swz<KB>(lane & 31)) * 16);
+
+  {
+    int src[A_PW];
+    load_src(t, src);
+    set_a(t, src);
+  }
+  set_b(t);
+  issue_a(0, 0);
+  issue_b(0, 0);
+  if (KT > 1) issue_b(1, 1);
+  for (;;) {
+    // The next tile's lookup and row indices, read while this tile's first K-tile is in flight
+    // (the wait at K-tile 0 covers them).
+    TileInfo tn;
+    const bool has_next = assign_tile<BM, BNO>(p, tn, vb + (int)gridDim.x);
+    int src_n[A_PW];
+    if (has_next) load_src(tn, src_n);
+    const int na = min(WM, max(0, (((t.rows + 31) >> 5) - wm + WAVES_M - 1) / WAVES_M));
+    f32x16 acc[WM][WN];
+    zero_acc(acc);
+    dispatch_na<WM>(na, [&](auto na_c) __attribute__((always_inline)) {
+      constexpr int NA = decltype(na_c)::value;
+      // Issue order per K-tile kt: A(kt+1), then B(kt+2); when A(kt) has landed only B(kt+1) can
+      // still be in flight (loads complete in issue order).
+      for (int kt = 0; kt < KT; ++kt) {
+        if (kt == 0 || kt + 1 >= KT) wait_vmcnt<0>();
+        else wait_vmcnt<B_PW>();
+        __syncthreads();  // every wave's part has landed; A stage (kt+1)%2 and B stage (kt+2)%3 are free
+        if (kt + 1 < KT) issue_a(kt + 1, (kt + 1) & 1);
+        if (kt + 2 < KT) issue_b(kt + 2, (kt + 2) % 3);
+        if (NA > 0)
+          dma_ktile<TI, WAVES_M, WAVES_N, WM, WN, KB, GLU, false, NA>(smem + (kt & 1) * A_BYTES,
+                                                                     smem + B_BASE + (kt % 3) * B_BYTES, fo, wm, wn,
+                                                                     lane, acc);
+      }
+    });
+    __syncthreads();  // every wave is done reading the pipeline stages
+    if (has_next) {
+      set_b(tn);
+      issue_b(0, 0);
+      if (KT > 1) issue_b(1, 1);
+    }
+    char* region = smem + wave * REGION;
+    if (p.c_dtype == LMOE_BF16)
+      epilogue_staged<TI, uint16_t, WAVES_M, WAVES_N, WM, WN, EPI, REGION, NTC>(p, t, acc, wm, wn, lane, na, region);
+    else
+      epilogue_staged<TI, float, WAVES_M, WAVES_N, WM, WN, EPI, REGION, NTC>(p, t, acc, wm, wn, lane, na, region);
+    if (!has_next) break;
+    __syncthreads();  // every wave is done with its staging region: the A stages take the next tile
+    set_a(tn, src_n);
+    issue_a(0, 0);
+    t = tn;
+    vb += (int)gridDim.x;
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -625,7 +793,7 @@ gemm_mx_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
   TileInfo t;
-  if (!assign_tile<BM, BNO>(p, t)) return;
+  if (!assign_tile<BM, BNO>(p, t, blockIdx.x)) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -826,7 +994,7 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) gemm_reg_kernel(GemmA
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   TileInfo t;
-  if (!assign_tile<BM, BNO>(p, t)) return;
+  if (!assign_tile<BM, BNO>(p, t, blockIdx.x)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1078,6 +1246,27 @@ int64_t grid_blocks(const GemmArgs& a, Epi epi) {
 constexpr int kDmaStages = 2;    // LDS stages of the DMA pipeline
 constexpr int kDmaKBytes = 128;  // bytes of every row per K-tile (64 bf16)
 
+// The persistent routed kernel covers grouped GEMMs over whole K (no K groups, splits or second
+// segment, A not wrapped) whose outputs take the staged epilogue.
+bool routed_persistent(const GemmArgs& a) {
+  const int vec = a.c_dtype == LMOE_BF16 ? 8 : 4;
+  return a.goff && !a.koff && !a.A2 && !a.b_kn && a.splits <= 1 && a.a_kwrap == a.K && a.N % vec == 0 &&
+         a.ldc % vec == 0;
+}
+
+// One workgroup per CU (a multiple of the XCD count), at most one per tile.
+template <typename TI, Epi EPI, bool NTC>
+hipError_t launch_routed(const GemmArgs& a, int64_t blocks, hipStream_t s) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t per_chip = cus >= kXcds ? cus / kXcds * kXcds : kXcds;
+  const dim3 grid((unsigned)(blocks < per_chip ? blocks : per_chip)), block(8 * kWave);
+  hipLaunchKernelGGL((gemm_routed_kernel<TI, 2, 4, 4, 2, kDmaKBytes, EPI, NTC>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename TI>
 hipError_t launch_big(const GemmArgs& a, Epi epi, hipStream_t s) {
   const int64_t blocks = grid_blocks<256, 256>(a, epi);
@@ -1095,6 +1284,7 @@ hipError_t launch_big(const GemmArgs& a, Epi epi, hipStream_t s) {
   // 0.90 ms; the backward's recomputed GEMM1 2.69 -> 2.58 ms; the dense GEMMs, whose B comes from
   // L2, the router's split-K halves and the [K, N]-B products lose 1-5 % with it and keep two stages).
   if (epi == Epi::Glu && a.goff) {  // routed GEMM1: W1 slices streamed with the non-temporal hint
+    if (routed_persistent(a)) return launch_routed<TI, Epi::Glu, false>(a, blocks, s);
     hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Glu, false, true, 1>), grid,
                        block, 0, s, a);
     return hipGetLastError();
@@ -1105,6 +1295,7 @@ hipError_t launch_big(const GemmArgs& a, Epi epi, hipStream_t s) {
     return hipGetLastError();
   }
   if (epi == Epi::Store && a.goff && !a.koff && !a.A2 && a.splits <= 1) {  // routed GEMM2: W2 in, y out, non-temporal
+    if (routed_persistent(a)) return launch_routed<TI, Epi::Store, true>(a, blocks, s);
     hipLaunchKernelGGL((gemm_dma_kernel<TI, 2, 4, 4, 2, kDmaStages, kDmaKBytes, Epi::Store, false, true, 1, true>),
                        grid, block, 0, s, a);
     return hipGetLastError();
