@@ -198,6 +198,50 @@ __device__ inline bool assign_tile(const GemmArgs& p, TileInfo& t, int vb) {
   return true;
 }
 
+// assign_tile for a grouped GEMM (no K groups) when this workgroup's previous tile was in group
+// g_hint: tile numbers only grow along a workgroup's walk, so the group is searched forward from
+// g_hint through a window of W entries of mtile_start read at once (one load round trip instead of
+// a binary search's chain of log2(G)), with the binary search as the fallback past the window.
+// mt_total is mtile_start[G]. On success g_hint holds the tile's group.
+template <int BM, int BNO>
+__device__ inline bool assign_tile_after(const GemmArgs& p, TileInfo& t, int vb, int mt_total, int& g_hint) {
+  constexpr int W = 16;
+  const int n_tiles = (int)ceil_div(p.N, BNO);
+  const int total = mt_total * n_tiles;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int loc = vb / kXcds;
+  if (loc >= per) return false;
+  const int lt = (vb % kXcds) * per + loc;
+  if (lt >= total) return false;
+  const int q = lt / n_tiles;
+  int v[W];
+#pragma unroll
+  for (int j = 0; j < W; ++j) v[j] = p.mtile_start[min(g_hint + 1 + j, p.G)];
+  int g = g_hint;  // mtile_start[g] <= q; the group is the last such g (mtile_start[G] > q)
+#pragma unroll
+  for (int j = 0; j < W; ++j) g += (g_hint + 1 + j < p.G && v[j] <= q) ? 1 : 0;
+  if (g == g_hint + W) {  // past the window
+    int lo = g, hi = p.G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.mtile_start[mid] <= q) lo = mid; else hi = mid;
+    }
+    g = lo;
+  }
+  g_hint = g;
+  t.g = g;
+  t.k0 = 0;
+  t.klen = p.K;
+  t.coff = 0;
+  const int ms0 = p.mtile_start[g];
+  const int mtg = p.mtile_start[g + 1] - ms0;
+  const int r = lt - n_tiles * ms0;
+  t.row0 = p.goff[g] + (r % mtg) * BM;
+  t.rows = min(BM, p.goff[g + 1] - t.row0);
+  t.n0 = (r / mtg) * BNO;
+  return true;
+}
+
 template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, Epi EPI>
 __device__ inline void epilogue(const GemmArgs& p, const TileInfo& t, f32x16 (&acc)[WM][WN], int wm, int wn,
                                 int lane, int na) {
@@ -623,6 +667,8 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
   int vb = blockIdx.x;
   TileInfo t;
   if (!assign_tile<BM, BNO>(p, t, vb)) return;
+  const int mt_total = p.mtile_start[p.G];
+  int g_hint = t.g;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -698,7 +744,7 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
     // The next tile's lookup and row indices, read while this tile's first K-tile is in flight
     // (the wait at K-tile 0 covers them).
     TileInfo tn;
-    const bool has_next = assign_tile<BM, BNO>(p, tn, vb + (int)gridDim.x);
+    const bool has_next = assign_tile_after<BM, BNO>(p, tn, vb + (int)gridDim.x, mt_total, g_hint);
     int src_n[A_PW];
     if (has_next) load_src(tn, src_n);
     const int na = min(WM, max(0, (((t.rows + 31) >> 5) - wm + WAVES_M - 1) / WAVES_M));
