@@ -455,6 +455,15 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
   constexpr int A_PW = BM / RPD / NW;      // DMA blocks per wave per K-tile
   constexpr int B_PW = BNB / RPD / NW;
   static_assert(A_PW * RPD * NW == BM && B_PW * RPD * NW == BNB, "DMA split");
+  // On the two-stage ring with [N, K] B, the upper half of the waves issues every DMA of a K-tile
+  // while the lower half goes straight to its MFMAs: a K-tile's 64 DMA instructions keep the
+  // address unit busy for about 1400 cycles, and with all eight waves issuing, every wave of a SIMD
+  // sat in that queue at once with the matrix pipe idle (measured at K3 prefill: 750-990 of
+  // 3300-3650 cycles per K-tile; shared GEMM1 0.917 -> 0.862 ms, down-projection 0.416 -> 0.388,
+  // up-projection 0.924 -> 0.853, outputs bit-identical).
+  constexpr bool DS = XB == 0 && !BKN && NW % 2 == 0;
+  constexpr int A_PWI = DS ? 2 * A_PW : A_PW;  // DMA blocks per issuing wave per K-tile
+  constexpr int B_PWI = DS ? 2 * B_PW : B_PW;
   static_assert(!GLU || BNO % RPD == 0, "a DMA block stays in one GLU half");
   constexpr int A_BYTES = BM * KB;  // one stage of A; the NS stages of A come first, then the NSB of B
   constexpr int B_BYTES = BNB * KB;
@@ -495,10 +504,12 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
   // The lane's source chunk for each DMA block of this wave (swizzled so that LDS slot s of row r
   // holds chunk s ^ swz<KB>(r)). A gathered row outside A gets an offset past the buffer end.
   const int lr = lane / (KB / 16), slot = lane % (KB / 16);
-  int a_voff[A_PW], b_voff[B_PW], a2_voff[A_PW], b2_voff[B_PW];
+  const bool issuer = !DS || wave >= NW / 2;
+  const int wi = DS ? (issuer ? wave - NW / 2 : 0) : wave;  // index among the issuing waves
+  int a_voff[A_PWI], b_voff[B_PWI], a2_voff[A_PWI], b2_voff[B_PWI];
 #pragma unroll
-  for (int i = 0; i < A_PW; ++i) {
-    const int r = (wave * A_PW + i) * RPD + lr;
+  for (int i = 0; i < A_PWI; ++i) {
+    const int r = (wi * A_PWI + i) * RPD + lr;
     const int ch = (slot ^ swz<KB>(r)) * 16;
     if (gather) {
       const int src = r < t.rows ? p.a_rows[t.row0 + r] : -1;
@@ -509,13 +520,13 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
     a2_voff[i] = r * (int)a_ld2 + ch;
   }
 #pragma unroll
-  for (int i = 0; i < B_PW; ++i) {
+  for (int i = 0; i < B_PWI; ++i) {
     if constexpr (BKN) {  // block j holds k-rows 2j and 2j + 1; lane l fills slot l % 32 of row 2j + l / 32
       const int k = 2 * (wave * B_PW + i) + lane / 32;
       b_voff[i] = k * (int)b_ld + (((lane % 32) ^ (k % 16)) * 16);
       b2_voff[i] = b_voff[i];
     } else {
-      const int r = (wave * B_PW + i) * RPD + lr;
+      const int r = (wi * B_PWI + i) * RPD + lr;
       const int ch = (slot ^ swz<KB>(r)) * 16;
       b_voff[i] = (r % BNO) * (int)b_ld + ch;
       b2_voff[i] = (r % BNO) * (int)b_ld2 + ch;
@@ -526,37 +537,39 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
 
   int ka = ka0;  // byte offset of the next issued K-tile inside A's (possibly wrapped) row
   auto issue_a = [&](int kt, int stage) __attribute__((always_inline)) {
+    if (!issuer) return;
     const unsigned base = lds0 + stage * A_BYTES;
     if (!seg2 || kt < KT1) {
 #pragma unroll
-      for (int i = 0; i < A_PW; ++i) dma16(a_desc, a_voff[i], ka, base + (wave * A_PW + i) * 1024);
+      for (int i = 0; i < A_PWI; ++i) dma16(a_desc, a_voff[i], ka, base + (wi * A_PWI + i) * 1024);
       ka += KB;
       if (ka == a_wrap) ka = 0;
     } else {
       const int kk = (kt - KT1) * KB;
 #pragma unroll
-      for (int i = 0; i < A_PW; ++i) dma16(a2_desc, a2_voff[i], kk, base + (wave * A_PW + i) * 1024);
+      for (int i = 0; i < A_PWI; ++i) dma16(a2_desc, a2_voff[i], kk, base + (wi * A_PWI + i) * 1024);
     }
   };
   auto issue_b = [&](int kt, int stage) __attribute__((always_inline)) {
+    if (!issuer) return;
     const unsigned base = lds0 + B_BASE + stage * B_BYTES;
     if (!seg2 || kt < KT1) {
 #pragma unroll
-      for (int i = 0; i < B_PW; ++i) {
-        const bool up = GLU && (wave * B_PW + i) * RPD >= BNO;
+      for (int i = 0; i < B_PWI; ++i) {
+        const bool up = GLU && (wi * B_PWI + i) * RPD >= BNO;
         const int soff = BKN ? kt * (KB / (int)sizeof(TI)) * (int)b_ld : kt * KB;
         if constexpr (NTB)
-          dma16_nt(up ? b_desc1 : b_desc0, b_voff[i], soff, base + (wave * B_PW + i) * 1024);
+          dma16_nt(up ? b_desc1 : b_desc0, b_voff[i], soff, base + (wi * B_PWI + i) * 1024);
         else
-          dma16(up ? b_desc1 : b_desc0, b_voff[i], soff, base + (wave * B_PW + i) * 1024);
+          dma16(up ? b_desc1 : b_desc0, b_voff[i], soff, base + (wi * B_PWI + i) * 1024);
       }
     } else {
       const int kk = (kt - KT1) * KB;
 #pragma unroll
-      for (int i = 0; i < B_PW; ++i) dma16(b2_desc, b2_voff[i], kk, base + (wave * B_PW + i) * 1024);
+      for (int i = 0; i < B_PWI; ++i) dma16(b2_desc, b2_voff[i], kk, base + (wi * B_PWI + i) * 1024);
     }
   };
-  constexpr int PER_TILE = A_PW + B_PW;  // DMA instructions per wave per K-tile
+  constexpr int PER_TILE = A_PWI + B_PWI;  // DMA instructions per issuing wave per K-tile
   auto wait_tiles_after = [&](int n) __attribute__((always_inline)) {
     if (NS > 4 && n >= 3) wait_vmcnt<3 * PER_TILE>();
     else if (NS > 3 && n == 2) wait_vmcnt<2 * PER_TILE>();
