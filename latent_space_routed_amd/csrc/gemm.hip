@@ -654,7 +654,7 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
 // take the next tile's data; the next tile's lookup and row indices are read while the current
 // tile's first K-tile is in flight. Same 256x256 tiles, swizzle, two A and three B stages as the
 // one-shot kernel (B one K-tile further ahead, with the non-temporal hint).
-template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, int KB, Epi EPI, bool NTC>
+template <typename TI, int WAVES_M, int WAVES_N, int WM, int WN, int KB, Epi EPI, bool NTC, bool IS = true>
 __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
     __attribute__((amdgpu_waves_per_eu(WAVES_M* WAVES_N / 4, WAVES_M* WAVES_N / 4)))  // one workgroup per CU
     gemm_routed_kernel(GemmArgs p) {
@@ -670,6 +670,11 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
   constexpr int B_PW = BNB / RPD / NW;
   static_assert(A_PW * RPD * NW == BM && B_PW * RPD * NW == BNB, "DMA split");
   static_assert(!GLU || BNO % RPD == 0, "a DMA block stays in one GLU half");
+  // IS: the upper half of the waves issues every DMA (as in the dense kernel), so that the lower
+  // half starts its MFMAs at once and never waits for the epilogue's stores to complete.
+  static_assert(!IS || NW % 2 == 0, "issue split needs an even wave count");
+  constexpr int A_PWI = IS ? 2 * A_PW : A_PW;  // DMA blocks per issuing wave per K-tile
+  constexpr int B_PWI = IS ? 2 * B_PW : B_PW;
   constexpr int A_BYTES = BM * KB;
   constexpr int B_BYTES = BNB * KB;
   constexpr int B_BASE = 2 * A_BYTES;
@@ -689,30 +694,32 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
   const bool gather = p.a_rows != nullptr;
   const int KT = p.K * (int)sizeof(TI) / KB;
   const int lr = lane / (KB / 16), slot = lane % (KB / 16);
+  const bool issuer = !IS || wave >= NW / 2;
+  const int wi = IS ? (issuer ? wave - NW / 2 : 0) : wave;  // index among the issuing waves
   const unsigned lds0 = __builtin_amdgcn_readfirstlane(
       (unsigned)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
 
   // Source row of each of the lane's A DMA blocks (gather: the row of A, -1 past the tile's rows).
-  auto load_src = [&](const TileInfo& tt, int (&src)[A_PW]) __attribute__((always_inline)) {
+  auto load_src = [&](const TileInfo& tt, int (&src)[A_PWI]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < A_PW; ++i) {
-      const int r = (wave * A_PW + i) * RPD + lr;
-      src[i] = gather ? (r < tt.rows ? p.a_rows[tt.row0 + r] : -1) : r;
+    for (int i = 0; i < A_PWI; ++i) {
+      const int r = (wi * A_PWI + i) * RPD + lr;
+      src[i] = gather ? (issuer && r < tt.rows ? p.a_rows[tt.row0 + r] : -1) : r;
     }
   };
   u32x4 a_desc, b_desc0, b_desc1;
-  int a_voff[A_PW], b_voff[B_PW];
+  int a_voff[A_PWI], b_voff[B_PWI];
 #pragma unroll
-  for (int i = 0; i < B_PW; ++i) {
-    const int r = (wave * B_PW + i) * RPD + lr;
+  for (int i = 0; i < B_PWI; ++i) {
+    const int r = (wi * B_PWI + i) * RPD + lr;
     b_voff[i] = (r % BNO) * (int)b_ld + ((slot ^ swz<KB>(r)) * 16);
   }
-  auto set_a = [&](const TileInfo& tt, const int (&src)[A_PW]) __attribute__((always_inline)) {
+  auto set_a = [&](const TileInfo& tt, const int (&src)[A_PWI]) __attribute__((always_inline)) {
     a_desc = gather ? make_desc(p.A, (int)(p.a_nrows * a_ld))
                     : make_desc(static_cast<const char*>(p.A) + (int64_t)tt.row0 * a_ld, (int)(tt.rows * a_ld));
 #pragma unroll
-    for (int i = 0; i < A_PW; ++i) {
-      const int r = (wave * A_PW + i) * RPD + lr;
+    for (int i = 0; i < A_PWI; ++i) {
+      const int r = (wi * A_PWI + i) * RPD + lr;
       const int ch = (slot ^ swz<KB>(r)) * 16;
       if (gather)
         a_voff[i] = (src[i] >= 0 && src[i] < p.a_nrows) ? src[i] * (int)a_ld + ch : kOutOfRange;
@@ -727,16 +734,18 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
     b_desc1 = GLU ? make_desc(Bb + (int64_t)(p.glu_up_off + tt.n0) * b_ld, (int)(ncols * b_ld)) : b_desc0;
   };
   auto issue_a = [&](int kt, int stage) __attribute__((always_inline)) {
+    if (!issuer) return;
     const unsigned base = lds0 + stage * A_BYTES;
 #pragma unroll
-    for (int i = 0; i < A_PW; ++i) dma16(a_desc, a_voff[i], kt * KB, base + (wave * A_PW + i) * 1024);
+    for (int i = 0; i < A_PWI; ++i) dma16(a_desc, a_voff[i], kt * KB, base + (wi * A_PWI + i) * 1024);
   };
   auto issue_b = [&](int kt, int stage) __attribute__((always_inline)) {
+    if (!issuer) return;
     const unsigned base = lds0 + B_BASE + stage * B_BYTES;
 #pragma unroll
-    for (int i = 0; i < B_PW; ++i) {
-      const bool up = GLU && (wave * B_PW + i) * RPD >= BNO;
-      dma16_nt(up ? b_desc1 : b_desc0, b_voff[i], kt * KB, base + (wave * B_PW + i) * 1024);
+    for (int i = 0; i < B_PWI; ++i) {
+      const bool up = GLU && (wi * B_PWI + i) * RPD >= BNO;
+      dma16_nt(up ? b_desc1 : b_desc0, b_voff[i], kt * KB, base + (wi * B_PWI + i) * 1024);
     }
   };
   constexpr int KS = KB / 32;
@@ -745,7 +754,7 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
   for (int s = 0; s < KS; ++s) fo[s] = (lane & 31) * KB + (((2 * s + (lane >> 5)) ^ swz<KB>(lane & 31)) * 16);
 
   {
-    int src[A_PW];
+    int src[A_PWI];
     load_src(t, src);
     set_a(t, src);
   }
@@ -758,7 +767,7 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
     // (the wait at K-tile 0 covers them).
     TileInfo tn;
     const bool has_next = assign_tile_after<BM, BNO>(p, tn, vb + (int)gridDim.x, mt_total, g_hint);
-    int src_n[A_PW];
+    int src_n[A_PWI];
     if (has_next) load_src(tn, src_n);
     const int na = min(WM, max(0, (((t.rows + 31) >> 5) - wm + WAVES_M - 1) / WAVES_M));
     f32x16 acc[WM][WN];
@@ -768,8 +777,10 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
       // Issue order per K-tile kt: A(kt+1), then B(kt+2); when A(kt) has landed only B(kt+1) can
       // still be in flight (loads complete in issue order).
       for (int kt = 0; kt < KT; ++kt) {
-        if (kt == 0 || kt + 1 >= KT) wait_vmcnt<0>();
-        else wait_vmcnt<B_PW>();
+        if (issuer) {  // the other waves issue no loads
+          if (kt == 0 || kt + 1 >= KT) wait_vmcnt<0>();
+          else wait_vmcnt<B_PWI>();
+        }
         __syncthreads();  // every wave's part has landed; A stage (kt+1)%2 and B stage (kt+2)%3 are free
         if (kt + 1 < KT) issue_a(kt + 1, (kt + 1) & 1);
         if (kt + 2 < KT) issue_b(kt + 2, (kt + 2) % 3);
