@@ -214,6 +214,21 @@ lmoe_status lmoe_combine_norm_up(const lmoe_shape* shape, const void* y_perm, co
                                  void* n_out, void* out, int32_t out_dtype, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* A9 alone: the combine and RMSNorm of lmoe_combine_norm_up (same arguments, same n_out). Its
+ * kernel holds few registers and no LDS to speak of, so it can run on one stream while another
+ * stream runs a GEMM that does not read n (the shared experts' GEMM1): its waves fit beside a
+ * GEMM workgroup on each CU. No workspace.                                                        */
+lmoe_status lmoe_combine_norm(const lmoe_shape* shape, const void* y_perm, const int32_t* slot_of_pair,
+                              const float* topk_w, const float* gamma, void* n_out, void* stream);
+
+/* A11 alone: the up-projection and shared-expert add of lmoe_combine_norm_up, from an n written
+ * by lmoe_combine_norm (same arguments, same out; workspace as for LMOE_CALL_COMBINE_NORM_UP).
+ * lmoe_combine_norm followed by lmoe_up_project on one stream equals lmoe_combine_norm_up bit for
+ * bit.                                                                                              */
+lmoe_status lmoe_up_project(const lmoe_shape* shape, const void* n, const void* w_up, const float* y_shared,
+                            const void* h_shared, const void* w2_shared, void* out, int32_t out_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* ================================================================================================
  * Backward pass (training). The pages train this layer ([vxz] 01-02, [slm] 训练基础设施) but
  * print no backward pass; these calls apply the chain rule to the forward above, step by step in

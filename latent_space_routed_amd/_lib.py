@@ -24,7 +24,8 @@ LMOE_CALL_BWD_UP, LMOE_CALL_BWD_COMBINE_NORM, LMOE_CALL_BWD_EXPERTS, LMOE_CALL_B
 # every symbol include/lmoe.h declares
 EXPORTS = ("lmoe_workspace_bytes", "lmoe_status_string", "lmoe_split_router", "lmoe_route", "lmoe_qb_histogram",
            "lmoe_qb_update", "lmoe_permute", "lmoe_grouped_situ_glu", "lmoe_grouped_situ_glu_noalloc",
-           "lmoe_pack_shared", "lmoe_combine_norm_up", "lmoe_bwd_transpose_weights", "lmoe_bwd_up",
+           "lmoe_pack_shared", "lmoe_combine_norm_up", "lmoe_combine_norm", "lmoe_up_project",
+           "lmoe_bwd_transpose_weights", "lmoe_bwd_up",
            "lmoe_bwd_combine_norm", "lmoe_bwd_router", "lmoe_bwd_experts", "lmoe_bwd_down", "lmoe_bwd_shared",
            "lmoe_mx_quantize", "lmoe_grouped_situ_glu_mx", "lmoe_profile_enable", "lmoe_profile_only",
            "lmoe_profile_reset", "lmoe_profile_collect", "lmoe_profile_get")
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
             "lmoe_pack_shared": (ctypes.c_int, [_S, _P, _P, _P, _P, _P]),
             "lmoe_combine_norm_up": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                     _P, ctypes.c_size_t, _P]),
+            "lmoe_combine_norm": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P]),
+            "lmoe_up_project": (ctypes.c_int, [_S, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
             "lmoe_bwd_transpose_weights": (ctypes.c_int, [_S] + [_P] * 9),
             "lmoe_bwd_up": (ctypes.c_int, [_S] + [_P] * 10 + [ctypes.c_size_t, _P]),
             "lmoe_bwd_combine_norm": (ctypes.c_int, [_S] + [_P] * 12 + [ctypes.c_size_t, _P]),
@@ -207,6 +210,20 @@ def lmoe_combine_norm_up(shape, y_perm, slot_of_pair, topk_w, gamma, w_up, y_sha
                                       _ptr(gamma), _ptr(w_up), _ptr(y_shared), _ptr(h_shared), _ptr(w2_shared),
                                       _ptr(n_out), _ptr(out), out_dtype, _ptr(workspace), _nbytes(workspace),
                                       _stream(stream)))
+
+
+def lmoe_combine_norm(shape, y_perm, slot_of_pair, topk_w, gamma, n_out, stream=None):
+    _check("lmoe_combine_norm",
+           lib().lmoe_combine_norm(ctypes.byref(shape), _ptr(y_perm), _ptr(slot_of_pair), _ptr(topk_w), _ptr(gamma),
+                                   _ptr(n_out), _stream(stream)))
+
+
+def lmoe_up_project(shape, n, w_up, y_shared, out, h_shared=None, w2_shared=None, workspace=None, stream=None):
+    out_dtype = LMOE_F32 if out.dtype == torch.float32 else LMOE_BF16
+    _check("lmoe_up_project",
+           lib().lmoe_up_project(ctypes.byref(shape), _ptr(n), _ptr(w_up), _ptr(y_shared), _ptr(h_shared),
+                                 _ptr(w2_shared), _ptr(out), out_dtype, _ptr(workspace), _nbytes(workspace),
+                                 _stream(stream)))
 
 
 def _call(name: str, shape, *args):

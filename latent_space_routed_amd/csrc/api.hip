@@ -436,10 +436,21 @@ lmoe_status lmoe_pack_shared(const lmoe_shape* sh, const void* w1s, const void* 
                                        w1s_packed, w2s_packed, static_cast<hipStream_t>(stream)));
 }
 
-lmoe_status lmoe_combine_norm_up(const lmoe_shape* sh, const void* y_perm, const int32_t* slot_of_pair,
-                                 const float* topk_w, const float* gamma, const void* w_up, const float* y_shared,
-                                 const void* h_shared, const void* w2_shared, void* n_out, void* out,
-                                 int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+lmoe_status lmoe_combine_norm(const lmoe_shape* sh, const void* y_perm, const int32_t* slot_of_pair,
+                              const float* topk_w, const float* gamma, void* n_out, void* stream) {
+  lmoe_status st = check_shape(sh);
+  if (st != LMOE_OK) return st;
+  if (sh->T == 0) return LMOE_OK;
+  if (!aligned16(y_perm) || !aligned4(slot_of_pair) || !aligned4(topk_w) || (gamma && !aligned4(gamma)) ||
+      !aligned16(n_out))
+    return LMOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_combine_norm(y_perm, slot_of_pair, topk_w, gamma, sh->T, sh->top_k, sh->d_latent,
+                                        sh->rms_eps, sh->act_dtype, n_out, static_cast<hipStream_t>(stream)));
+}
+
+lmoe_status lmoe_up_project(const lmoe_shape* sh, const void* n, const void* w_up, const float* y_shared,
+                            const void* h_shared, const void* w2_shared, void* out, int32_t out_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   lmoe_status st = check_shape(sh);
   if (st != LMOE_OK) return st;
   if (out_dtype != LMOE_F32 && out_dtype != sh->act_dtype) return LMOE_ERR_INVALID_ARGUMENT;
@@ -447,17 +458,12 @@ lmoe_status lmoe_combine_norm_up(const lmoe_shape* sh, const void* y_perm, const
   if ((h_shared != nullptr) != (w2_shared != nullptr) || (h_shared && y_shared)) return LMOE_ERR_INVALID_ARGUMENT;
   const int Ss = sh->n_shared * sh->inter_shared;
   if (h_shared && Ss < 64) return LMOE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(y_perm) || !aligned4(slot_of_pair) || !aligned4(topk_w) || (gamma && !aligned4(gamma)) ||
-      !aligned16(w_up) || (y_shared && !aligned4(y_shared)) || (h_shared && !aligned16(h_shared)) ||
-      (w2_shared && !aligned16(w2_shared)) || !aligned16(n_out) || !aligned16(out))
+  if (!aligned16(n) || !aligned16(w_up) || (y_shared && !aligned4(y_shared)) || (h_shared && !aligned16(h_shared)) ||
+      (w2_shared && !aligned16(w2_shared)) || !aligned16(out))
     return LMOE_ERR_INVALID_ARGUMENT;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const int T = sh->T, D = sh->d_model, L = sh->d_latent;
-  st = hip_status(launch_combine_norm(y_perm, slot_of_pair, topk_w, gamma, T, sh->top_k, L, sh->rms_eps,
-                                      sh->act_dtype, n_out, s));
-  if (st != LMOE_OK) return st;
   GemmArgs a = gemm_args();
-  a.A = n_out;
+  a.A = n;
   a.lda = L;
   a.a_kwrap = L;
   a.a_nrows = T;
@@ -483,7 +489,28 @@ lmoe_status lmoe_combine_norm_up(const lmoe_shape* sh, const void* y_perm, const
   const SplitPlan sp = up_plan(sh, h_shared != nullptr);
   float* part = split_region(sp, T, D, workspace, workspace_bytes, 0);
   return hip_status(run_gemm(a, sh->act_dtype, y_shared ? Epi::AddF32 : Epi::Store, dense_shape(T, ceil_div(D, 256)),
-                             sp, part, s));
+                             sp, part, static_cast<hipStream_t>(stream)));
+}
+
+lmoe_status lmoe_combine_norm_up(const lmoe_shape* sh, const void* y_perm, const int32_t* slot_of_pair,
+                                 const float* topk_w, const float* gamma, const void* w_up, const float* y_shared,
+                                 const void* h_shared, const void* w2_shared, void* n_out, void* out,
+                                 int32_t out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  lmoe_status st = check_shape(sh);
+  if (st != LMOE_OK) return st;
+  if (out_dtype != LMOE_F32 && out_dtype != sh->act_dtype) return LMOE_ERR_INVALID_ARGUMENT;
+  if (sh->T == 0) return LMOE_OK;
+  if ((h_shared != nullptr) != (w2_shared != nullptr) || (h_shared && y_shared)) return LMOE_ERR_INVALID_ARGUMENT;
+  const int Ss = sh->n_shared * sh->inter_shared;
+  if (h_shared && Ss < 64) return LMOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y_perm) || !aligned4(slot_of_pair) || !aligned4(topk_w) || (gamma && !aligned4(gamma)) ||
+      !aligned16(w_up) || (y_shared && !aligned4(y_shared)) || (h_shared && !aligned16(h_shared)) ||
+      (w2_shared && !aligned16(w2_shared)) || !aligned16(n_out) || !aligned16(out))
+    return LMOE_ERR_INVALID_ARGUMENT;
+  st = lmoe_combine_norm(sh, y_perm, slot_of_pair, topk_w, gamma, n_out, stream);
+  if (st != LMOE_OK) return st;
+  return lmoe_up_project(sh, n_out, w_up, y_shared, h_shared, w2_shared, out, out_dtype, workspace, workspace_bytes,
+                         stream);
 }
 
 lmoe_status lmoe_mx_quantize(const lmoe_shape* sh, int32_t fmt, int64_t rows, int32_t K, const void* x, void* codes,

@@ -120,6 +120,15 @@ def test_pointer_validation_before_any_launch(lib):
     # combine: y_shared and the folded shared pair are exclusive
     assert lib.lmoe_combine_norm_up(ctypes.byref(sh), fake, fake, fake, null, fake, fake, fake, fake, fake, fake, 0,
                                     null, 0, null) == C.LMOE_ERR_INVALID_ARGUMENT
+    # the split calls check the same arguments
+    assert lib.lmoe_up_project(ctypes.byref(sh), fake, fake, fake, fake, fake, fake, 0, null, 0, null) == \
+        C.LMOE_ERR_INVALID_ARGUMENT
+    assert lib.lmoe_up_project(ctypes.byref(sh), misaligned, fake, null, null, null, fake, 0, null, 0, null) == \
+        C.LMOE_ERR_INVALID_ARGUMENT
+    assert lib.lmoe_up_project(ctypes.byref(sh), fake, fake, null, null, null, fake, 7, null, 0, null) == \
+        C.LMOE_ERR_INVALID_ARGUMENT
+    assert lib.lmoe_combine_norm(ctypes.byref(sh), misaligned, fake, fake, null, fake, null) == \
+        C.LMOE_ERR_INVALID_ARGUMENT
 
 
 def test_empty_batch_is_a_no_op(lib):
@@ -130,6 +139,8 @@ def test_empty_batch_is_a_no_op(lib):
     assert lib.lmoe_qb_histogram(ctypes.byref(sh), null, null, null, null, null, null) == C.LMOE_OK
     assert lib.lmoe_combine_norm_up(ctypes.byref(sh), null, null, null, null, null, null, null, null, null, null, 0,
                                     null, 0, null) == C.LMOE_OK
+    assert lib.lmoe_combine_norm(ctypes.byref(sh), null, null, null, null, null, null) == C.LMOE_OK
+    assert lib.lmoe_up_project(ctypes.byref(sh), null, null, null, null, null, null, 0, null, 0, null) == C.LMOE_OK
 
 
 def test_backward_workspace_and_validation(lib):

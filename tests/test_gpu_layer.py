@@ -200,6 +200,24 @@ def test_deterministic(run):
             np.testing.assert_array_equal(host(b[name]), g[name], err_msg=name)
 
 
+def test_side_stream_and_split_calls_bit_identical(run):
+    """With the side stream on, the fused layer runs the shared GEMM1 on it beside lmoe_combine_norm,
+    then joins for lmoe_up_project; off (the default), it calls lmoe_combine_norm_up on one stream.
+    Both give the same n, h_s and out bit for bit (same kernels, same per-stream order)."""
+    cfg, inp, layer, x, g, ref = run
+    if not g["fused"] or cfg.n_shared == 0:
+        pytest.skip("the side stream is used on the fused path with shared experts")
+    side, _ = device_layer(cfg, inp)
+    side.overlap_shared = True
+    side.bias.copy_(layer.bias)
+    layer.overlap_shared = False
+    b1 = layer.forward(x, accumulate_hist=False)
+    b2 = side.forward(x, accumulate_hist=False)
+    torch.cuda.synchronize()
+    for name in ("n", "h_s", "out"):
+        np.testing.assert_array_equal(host(b2[name]), host(b1[name]), err_msg=name)
+
+
 # ---------------------------------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------------------------------
