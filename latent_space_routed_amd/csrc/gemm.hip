@@ -839,7 +839,7 @@ __device__ inline void dma4(const u32x4& desc, int voff, int soff, unsigned lds_
 constexpr int kMxK = 128;     // k per K-tile of the MX pipeline
 constexpr int kMxStages = 3;  // 150 KB of LDS: two K-tiles in flight while a third is consumed
 
-template <int WAVES_M, int WAVES_N, int WM, int WN, int NS, Epi EPI>
+template <int WAVES_M, int WAVES_N, int WM, int WN, int NS, Epi EPI, bool DS = true>
 __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_mx_kernel(GemmArgs p) {
   constexpr int NW = WAVES_M * WAVES_N;
@@ -856,6 +856,11 @@ gemm_mx_kernel(GemmArgs p) {
   static_assert(!GLU || BNO % RPB == 0, "a DMA block stays in one GLU half");
   constexpr int SA_N = BM / 64, SB_N = BNB / 64;  // scale dword DMAs per K-tile (64 rows each)
   static_assert(SA_N + SB_N == NW, "one scale DMA per wave");
+  // DS: as in the bf16 pipeline, the upper half of the waves issues every DMA of a K-tile (twice
+  // the blocks and two scale DMAs each) while the lower half goes straight to its MFMAs (the MX
+  // GEMM1 only: measured at K3 prefill, 4-5 % faster there and 6 % slower on GEMM2).
+  static_assert(!DS || NW % 2 == 0, "issue split needs an even wave count");
+  constexpr int NI = DS ? 2 : 1;  // share of the K-tile's DMA blocks per issuing wave
   static_assert(!GLU || BNO % 64 == 0, "a scale DMA stays in one GLU half");
   constexpr int A_BYTES = BM * KA, B_BYTES = BNB * KBB;
   constexpr int STAGE = A_BYTES + B_BYTES + (BM + BNB) * 4;
@@ -891,12 +896,14 @@ gemm_mx_kernel(GemmArgs p) {
     const int src = r < t.rows ? p.a_rows[t.row0 + r] : -1;
     return (src >= 0 && src < p.a_nrows) ? src : -1;
   };
-  int a_voff[A_PW], b_voff[B_PW];
+  const bool issuer = !DS || wave >= NW / 2;
+  const int wi = DS ? (issuer ? wave - NW / 2 : 0) : wave;  // index among the issuing waves
+  int a_voff[NI * A_PW], b_voff[NI * B_PW];
   {
     const int lr = lane / (KA / 16), slot = lane % (KA / 16);
 #pragma unroll
-    for (int i = 0; i < A_PW; ++i) {
-      const int r = (wave * A_PW + i) * RPA + lr;
+    for (int i = 0; i < NI * A_PW; ++i) {
+      const int r = (wi * NI * A_PW + i) * RPA + lr;
       const int src = a_src(r);
       a_voff[i] = src >= 0 ? src * (int)a_ld + ((slot ^ swz<KA>(r)) * 16) : kOutOfRange;
     }
@@ -904,38 +911,45 @@ gemm_mx_kernel(GemmArgs p) {
   {
     const int lr = lane / (KBB / 16), slot = lane % (KBB / 16);
 #pragma unroll
-    for (int i = 0; i < B_PW; ++i) {
-      const int r = (wave * B_PW + i) * RPB + lr;
+    for (int i = 0; i < NI * B_PW; ++i) {
+      const int r = (wi * NI * B_PW + i) * RPB + lr;
       b_voff[i] = (r % BNO) * (int)b_ld + ((slot ^ swz<KBB>(r)) * 16);
     }
   }
-  // scale DMA of this wave: A rows [64 w, 64 w + 64) for w < SA_N, else B rows [64 (w - SA_N), ...)
-  u32x4 s_desc;
-  int s_voff;
-  if (wave < SA_N) {
-    const int src = a_src(wave * 64 + lane);
-    s_desc = as_desc;
-    s_voff = src >= 0 ? src * (int)s_ld : kOutOfRange;
-  } else {
-    const int r = (wave - SA_N) * 64 + lane;
-    s_desc = (GLU && (wave - SA_N) * 64 >= BNO) ? bs_desc1 : bs_desc0;
-    s_voff = (r % BNO) * (int)s_ld;
+  // scale DMAs of this wave: scale block sw covers A rows [64 sw, 64 sw + 64) for sw < SA_N, else
+  // B rows [64 (sw - SA_N), ...); an issuing wave takes blocks NI wi .. NI wi + NI - 1
+  u32x4 s_desc[NI];
+  int s_voff[NI];
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    const int sw = NI * wi + q;
+    if (sw < SA_N) {
+      const int src = a_src(sw * 64 + lane);
+      s_desc[q] = as_desc;
+      s_voff[q] = src >= 0 ? src * (int)s_ld : kOutOfRange;
+    } else {
+      const int r = (sw - SA_N) * 64 + lane;
+      s_desc[q] = (GLU && (sw - SA_N) * 64 >= BNO) ? bs_desc1 : bs_desc0;
+      s_voff[q] = (r % BNO) * (int)s_ld;
+    }
   }
   const unsigned lds0 = __builtin_amdgcn_readfirstlane(
       (unsigned)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
 
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    if (!issuer) return;
     const unsigned base = lds0 + stage * STAGE;
 #pragma unroll
-    for (int i = 0; i < A_PW; ++i) dma16(a_desc, a_voff[i], kt * KA, base + (wave * A_PW + i) * 1024);
+    for (int i = 0; i < NI * A_PW; ++i) dma16(a_desc, a_voff[i], kt * KA, base + (wi * NI * A_PW + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < B_PW; ++i) {
-      const bool up = GLU && (wave * B_PW + i) * RPB >= BNO;
-      dma16(up ? b_desc1 : b_desc0, b_voff[i], kt * KBB, base + A_BYTES + (wave * B_PW + i) * 1024);
+    for (int i = 0; i < NI * B_PW; ++i) {
+      const bool up = GLU && (wi * NI * B_PW + i) * RPB >= BNO;
+      dma16(up ? b_desc1 : b_desc0, b_voff[i], kt * KBB, base + A_BYTES + (wi * NI * B_PW + i) * 1024);
     }
-    dma4(s_desc, s_voff, kt * 4, base + A_BYTES + B_BYTES + wave * 256);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) dma4(s_desc[q], s_voff[q], kt * 4, base + A_BYTES + B_BYTES + (NI * wi + q) * 256);
   };
-  constexpr int PER_TILE = A_PW + B_PW + 1;
+  constexpr int PER_TILE = NI * (A_PW + B_PW + 1);  // DMA instructions per issuing wave per K-tile
   auto wait_tiles_after = [&](int n) __attribute__((always_inline)) {
     if (NS > 3 && n >= 2) wait_vmcnt<2 * PER_TILE>();
     else if (NS > 2 && n == 1) wait_vmcnt<PER_TILE>();
@@ -1547,7 +1561,9 @@ hipError_t launch_gemm_mx(const GemmArgs& a, Epi epi, hipStream_t s) {
   if (epi == Epi::Glu)
     hipLaunchKernelGGL((gemm_mx_kernel<2, 4, 4, 2, kMxStages, Epi::Glu>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_mx_kernel<2, 4, 4, 2, kMxStages, Epi::Store>), grid, block, 0, s, a);
+    // GEMM2's short K loop (4 K-tiles at K3 shape) loses with the issue split: 0.55-0.58 ms with
+    // every wave issuing against 0.59-0.61 with the split; GEMM1 gains (0.66-0.69 vs 0.68-0.72)
+    hipLaunchKernelGGL((gemm_mx_kernel<2, 4, 4, 2, kMxStages, Epi::Store, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
