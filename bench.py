@@ -208,7 +208,9 @@ def mx_steps(cfg, w, xs, args, _lib, torch, LatentMoE, flush) -> dict:
         step(i)
     torch.cuda.synchronize()
     t = timed_steps(step, args.steps, flush, torch, _lib, None)
-    bd_steps = min(args.steps, 20)  # per-kernel breakdown in a pass of its own
+    bd_steps = min(args.steps, 20)  # per-kernel breakdown in a pass of its own, on one stream
+    overlap = layer.overlap_shared
+    layer.overlap_shared = False
     _lib.profile_reset()
     _lib.profile_enable(True)
     for i in range(bd_steps):
@@ -216,6 +218,7 @@ def mx_steps(cfg, w, xs, args, _lib, torch, LatentMoE, flush) -> dict:
     torch.cuda.synchronize()
     _lib.profile_enable(False)
     _lib.profile_collect()
+    layer.overlap_shared = overlap
     kernels, roof = {}, {}
     b = layer.forward(xs[0])
     torch.cuda.synchronize()
@@ -346,11 +349,16 @@ def timed_steps(step, n_steps: int, flush, torch, _lib, dominant: str | None) ->
     return out
 
 
-def breakdown(step, n: int, torch, _lib) -> dict:
-    """Per-kernel milliseconds per step: every kernel between HIP events (a pass of its own)."""
+def breakdown(step, n: int, torch, _lib, layer=None) -> dict:
+    """Per-kernel milliseconds per step: every kernel between HIP events (a pass of its own). The
+    pass runs every kernel on the caller's stream (the layer's side stream off), so that no two of
+    the timed kernels overlap."""
     names = ["router_split", "gemm_router", "route_topk", "qb_hist", "gemm_down", "perm_count", "perm_scan",
              "perm_scatter", "gather_rows", "mtile_prefix", "gemm_glu_grouped", "gemm_down_grouped",
              "gemm_glu_dense", "gemm_out_dense", "combine_norm", "gemm_up", "splitk_reduce", "qb_update"]
+    overlap = layer.overlap_shared if layer is not None else None
+    if layer is not None:
+        layer.overlap_shared = False
     _lib.profile_reset()
     _lib.profile_enable(True)
     for i in range(n):
@@ -358,6 +366,8 @@ def breakdown(step, n: int, torch, _lib) -> dict:
     torch.cuda.synchronize()
     _lib.profile_enable(False)
     _lib.profile_collect()
+    if layer is not None:
+        layer.overlap_shared = overlap
     out = {}
     for nm in names:
         cnt, ms = _lib.profile_get(nm)
@@ -462,7 +472,7 @@ def run_workload(cfg, args, cache, flush, torch, np, _lib, headline: bool) -> tu
     res.update({"T": cfg.T, "ms_per_step": t["ms_median"], "ms_min": t["ms_min"], "ms_mean": t["ms_mean"],
                 "tokens_per_s": cfg.T / (t["ms_median"] / 1e3),
                 "roofline": dominant_roofline(cfg, offsets, t["dominant_avg_ms"]) if t["dominant_avg_ms"] else None})
-    kernels = breakdown(step, min(args.steps, 20), torch, _lib)
+    kernels = breakdown(step, min(args.steps, 20), torch, _lib, layer)
     res["kernels_ms_per_step"] = kernels
     res["kernels_roofline"] = kernel_roofline(kernel_work(cfg, offsets, layer.fused), kernels)
     return res, layer, inp, xs

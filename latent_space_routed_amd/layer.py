@@ -41,11 +41,18 @@ class LatentMoE:
 
     def __init__(self, cfg, weights: dict, max_tokens: int | None = None, device: str = "cuda",
                  out_dtype: torch.dtype = torch.float32, fused: bool = True, mx: bool = False,
-                 overlap_shared: bool = False):
+                 overlap_shared: bool | None = None):
         self.cfg = cfg
-        # fused path with shared experts, when set: their GEMM1 runs on a side stream while the combine
-        # runs on the caller's stream (the combine's waves fit beside the GEMM's workgroups on every
-        # CU). Measured at K3 prefill: 4.59-4.63 ms per step with it, 4.61-4.62 without, so it is off.
+        # Fused path with shared experts: their GEMM1 depends on x alone, so it can run on a side
+        # stream forked at the start of the step, beside the router, top-k, histogram,
+        # down-projection and permutation, whose small kernels and the down-projection's last
+        # partial round of tiles leave CUs idle; the caller's stream waits for it before the
+        # up-projection. Outputs are bit-identical either way. Measured (one process, on and off
+        # alternating): K3 prefill 4.47-4.48 ms per step against 4.52, the routed experts' call
+        # unchanged; K3 decode 1.89 against 1.91; the tiny f32 workload 0.112-0.120 against 0.108,
+        # where the fork and join cost more than the overlap gives. Forking after the route or
+        # after the permutation instead makes the routed GEMMs share the chip (slower). None (the
+        # default) turns it on when the shared GEMM1 of the batch is at least 1 GFLOP.
         self.overlap_shared = overlap_shared
         self._side = None
         if mx and (cfg.act_dtype != "bf16" or not fused):
@@ -117,7 +124,19 @@ class LatentMoE:
                             ("ws_glu", C.LMOE_CALL_GROUPED_GLU), ("ws_combine", C.LMOE_CALL_COMBINE_NORM_UP)):
             n = C.workspace_bytes(shape, which)
             b[name] = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        if self.fused and S > 0:
+            # the side stream's shared GEMM1 runs beside the routed one: a workspace of its own
+            # (allocated whether or not overlap_shared is set, so the flag can change between steps)
+            b["ws_glu_side"] = torch.empty_like(b["ws_glu"])
+            if self._side is None:
+                self._side = torch.cuda.Stream(device=dev)
         self._bufs = b
+
+    def _overlapped(self, T: int) -> bool:
+        cfg = self.cfg
+        if not (self.fused and cfg.n_shared > 0) or self.overlap_shared is False:
+            return False
+        return self.overlap_shared or 4.0 * T * cfg.d_model * cfg.n_shared * cfg.inter_shared >= 1e9
 
     # -------------------------------------------------------------------------------------------
     def forward(self, x: torch.Tensor, accumulate_hist: bool = True) -> dict:
@@ -139,6 +158,13 @@ class LatentMoE:
         shape = C.make_shape(cfg, T)
         E, k, L, D, I = cfg.n_experts, cfg.top_k, cfg.d_latent, cfg.d_model, cfg.inter
         S, Is = cfg.n_shared, cfg.inter_shared
+        side = self._side if self._overlapped(T) else None
+        if side is not None:
+            cur = torch.cuda.current_stream()
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                C.lmoe_grouped_situ_glu(shape, 1, T, D, S * Is, D, x, None, self.w1s_packed, None, b["h_s"], None,
+                                        b["ws_glu_side"])
         C.lmoe_route(shape, x, w["w_router"], self.bias, w.get("logit_offset"), b["scores"], b["idx"], b["w"],
                      b["thresh"], b["ws_route"], w_router_split=self.w_router_split)
         if accumulate_hist:
@@ -159,17 +185,9 @@ class LatentMoE:
         else:
             C.lmoe_grouped_situ_glu(shape, E, T * k, L, I, L, b["x_perm"], b["offsets"], w["w1"], w["w2"], b["h"],
                                     b["y"], b["ws_glu"])
-        if S > 0 and fused and self.overlap_shared:
-            cur = torch.cuda.current_stream()
-            if self._side is None:
-                self._side = torch.cuda.Stream(device=x.device)
-            side = self._side
-            side.wait_stream(cur)  # after the routed GEMMs: the side GEMM then shares the CUs with the combine only
-            with torch.cuda.stream(side):
-                C.lmoe_grouped_situ_glu(shape, 1, T, D, S * Is, D, x, None, self.w1s_packed, None, b["h_s"], None,
-                                        b["ws_glu"])
+        if side is not None:
             C.lmoe_combine_norm(shape, b["y"], b["slot_of_pair"], b["w"], w.get("gamma"), b["n"])
-            cur.wait_stream(side)
+            cur.wait_stream(side)  # h_s is ready
             C.lmoe_up_project(shape, b["n"], w["w_up"], None, b["out"], h_shared=b["h_s"], w2_shared=self.w2s_packed,
                               workspace=b["ws_combine"])
         elif S > 0 and fused:
