@@ -198,7 +198,7 @@ def mx_work(cfg, offsets) -> dict:
 def mx_steps(cfg, w, xs, args, _lib, torch, LatentMoE, flush) -> dict:
     """Forward steps with the routed experts on MX operands (MXFP4 weights, MXFP8 activations), timed
     like the headline steps."""
-    layer = LatentMoE(cfg, w, mx=True)
+    layer = LatentMoE(cfg, w, mx=True, overlap_shared=False if args.one_stream else None)
 
     def step(i):
         layer.forward(xs[i % 2])
@@ -450,7 +450,7 @@ def run_workload(cfg, args, cache, flush, torch, np, _lib, headline: bool) -> tu
 
     log(f"[bench] {cfg.name}: inputs")
     inp, w, xs = setup_workload(cfg, cache, torch, np)
-    layer = LatentMoE(cfg, w)
+    layer = LatentMoE(cfg, w, overlap_shared=False if args.one_stream else None)
     res = {}
     if cfg.qb_updates > 1:
         log(f"[bench] {cfg.name}: {cfg.qb_updates} QB updates over distinct batches")
@@ -494,6 +494,9 @@ def main() -> int:
                     help="skip the forward steps with MX routed experts (reported under 'mx')")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other workloads (reported under 'configs')")
+    ap.add_argument("--one-stream", action="store_true",
+                    help="run the shared experts' GEMM1 on the caller's stream too (per-kernel traces: no kernel "
+                         "shares the chip with another)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB 5 times (counter calibration)")
     args = ap.parse_args()
