@@ -142,8 +142,8 @@ hipError_t launch_t(const void* y, const int32_t* sp, const float* w, const floa
 // Lean variant: four waves per token (a workgroup of 256 lanes), lane g owning the 16-byte chunks
 // g + 256 i of the latent row, R rows in flight per step. Few registers per wave (about 60 at K3
 // shape against 129 for one wave per token), so its waves fit beside a resident GEMM workgroup
-// (which leaves 80 VGPRs and 32 KB of LDS per SIMD) and the combine can run concurrently with the
-// shared experts' GEMM on another stream. The four waves' partial sums of squares meet in LDS.
+// (which leaves 80 VGPRs and 32 KB of LDS per SIMD) when a caller runs the combine beside a dense
+// GEMM on another stream. The four waves' partial sums of squares meet in LDS.
 template <typename T, int CPW, int R>
 __global__ void __launch_bounds__(256) combine_norm_lean_kernel(const T* __restrict__ y,
                                                                 const int32_t* __restrict__ slot_of_pair,

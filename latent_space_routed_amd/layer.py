@@ -126,7 +126,8 @@ class LatentMoE:
             n = C.workspace_bytes(shape, which)
             b[name] = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
         if self.fused and S > 0:
-            # the side stream's shared GEMM1 runs beside the routed one: a workspace of its own
+            # the side stream's shared GEMM1 runs beside the router's and the down-projection's
+            # calls, which have workspaces of their own: it gets one too
             # (allocated whether or not overlap_shared is set, so the flag can change between steps)
             b["ws_glu_side"] = torch.empty_like(b["ws_glu"])
             if self._side is None:
