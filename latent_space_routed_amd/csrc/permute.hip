@@ -2,12 +2,15 @@
 // device (no host synchronisation, static shapes: [slm] 训练基础设施), then a gather of latent rows.
 //
 //   count   : per 256-token chunk, how many of its tokens chose each expert      -> cc[chunk][e]
-//             (every wave marks its 64 tokens' experts in an LDS bitmask per expert; the count is
-//             the masks' popcount, so a token that lists an expert twice counts once)
+//             (the chunk's 64-token blocks mark their tokens' experts in an LDS bitmask per
+//             expert, four lanes per token; the count is the masks' popcount, so a token that lists
+//             an expert twice counts once)
 //   scan    : exclusive prefix over chunks (in place) and over experts          -> offsets[E+1]
-//   scatter : per chunk, every wave marks its 64 tokens' experts in an LDS bitmask per expert; the
-//             rank of token t inside expert e is offsets[e] + cc[chunk][e] + (tokens of earlier
-//             waves) + popcount(mask_e & lanes below t). Tokens therefore ascend inside an expert.
+//   scatter : per chunk, one lane per token marks the masks in pair order (a pair whose bit is
+//             already set repeats an expert and is dropped) and leaves each pair's expert in LDS;
+//             then four lanes per token rank and store: the rank of token t inside expert e is
+//             offsets[e] + cc[chunk][e] + (tokens of earlier 64-token blocks) + popcount(mask_e &
+//             lanes below t). Tokens therefore ascend inside an expert.
 //   gather  : one wave per token loads its latent row once and writes it to its k sorted rows.
 // An expert index outside [0, E), or one that a token lists a second time, drops the pair: its slot is
 // -1, it takes no sorted row, and later kernels skip it. expert_offsets[E] is then the number of
@@ -20,23 +23,29 @@ namespace lmoe {
 namespace {
 
 constexpr int kMaxExpertsLds = 2048;  // the library's largest expert count
+constexpr int kMaxTopKLds = 64;       // and its largest k
 
-__global__ void __launch_bounds__(kPermChunk) perm_count_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
-                                                                 int32_t* __restrict__ cc) {
-  extern __shared__ unsigned long long marks[];  // [4][E]: bit l of marks[w][e] = token 64 w + l chose e
+constexpr int kPermLanes = 4;                           // lanes per token in the count and the ranking
+constexpr int kPermThreads = kPermChunk * kPermLanes;  // threads of a count or scatter workgroup
+
+__global__ void __launch_bounds__(kPermThreads) perm_count_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                                                                   int32_t* __restrict__ cc) {
+  extern __shared__ unsigned long long marks[];  // [4][E]: bit l of marks[b][e] = token 64 b + l chose e
   constexpr int W = kPermChunk / 64;
-  for (int i = threadIdx.x; i < W * E; i += kPermChunk) marks[i] = 0ull;
+  for (int i = threadIdx.x; i < W * E; i += kPermThreads) marks[i] = 0ull;
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * kPermChunk + threadIdx.x;
+  // lane group g takes pairs g, g + 4, ... of token ti (a wave holds 64 consecutive tokens)
+  const int ti = threadIdx.x % kPermChunk, g = threadIdx.x / kPermChunk;
+  const int lane = ti & 63, tb = ti >> 6;
+  const int64_t t = (int64_t)blockIdx.x * kPermChunk + ti;
   if (t < T) {
-    for (int j = 0; j < k; ++j) {
+    for (int j = g; j < k; j += kPermLanes) {
       const int e = idx[t * k + j];
-      if (e >= 0 && e < E) atomicOr(&marks[wave * E + e], 1ull << lane);
+      if (e >= 0 && e < E) atomicOr(&marks[tb * E + e], 1ull << lane);
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kPermChunk) {
+  for (int e = threadIdx.x; e < E; e += kPermThreads) {
     int n = 0;
 #pragma unroll
     for (int w = 0; w < W; ++w) n += __popcll(marks[w * E + e]);
@@ -89,61 +98,59 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ c
   if (threadIdx.x == 1023) offsets[E] = run;
 }
 
-__global__ void __launch_bounds__(kPermChunk) perm_scatter_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
-                                                                   const int32_t* __restrict__ cc,
-                                                                   const int32_t* __restrict__ offsets,
-                                                                   int32_t* __restrict__ sorted_token,
-                                                                   int32_t* __restrict__ slot_of_pair) {
-  extern __shared__ unsigned long long bits[];  // [4][E] masks, then [E] i32 bases of this chunk
+__global__ void __launch_bounds__(kPermThreads) perm_scatter_kernel(const int32_t* __restrict__ idx, int T, int E,
+                                                                     int k, const int32_t* __restrict__ cc,
+                                                                     const int32_t* __restrict__ offsets,
+                                                                     int32_t* __restrict__ sorted_token,
+                                                                     int32_t* __restrict__ slot_of_pair) {
+  // [4][E] masks, then [E] i32 bases of this chunk, then [256][k] i32: each pair's expert, -1 if dropped
+  extern __shared__ unsigned long long bits[];
   constexpr int W = kPermChunk / 64;
   int32_t* base_e = reinterpret_cast<int32_t*>(bits + W * E);
-  for (int i = threadIdx.x; i < W * E; i += kPermChunk) bits[i] = 0ull;
+  int32_t* pair_e = base_e + E;
+  for (int i = threadIdx.x; i < W * E; i += kPermThreads) bits[i] = 0ull;
   // the chunk's first slot in every expert, read once with coalesced loads
-  for (int e = threadIdx.x; e < E; e += kPermChunk) base_e[e] = offsets[e] + cc[(int64_t)blockIdx.x * E + e];
+  for (int e = threadIdx.x; e < E; e += kPermThreads) base_e[e] = offsets[e] + cc[(int64_t)blockIdx.x * E + e];
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * kPermChunk + threadIdx.x;
-  const bool live = t < T;
-  // The token's pairs are handled KB at a time: their expert indices, then the expert bases, are
-  // loaded together, so a pair's loads do not wait on the previous pair's stores. The pairs of a
-  // token set their bits in order, so a pair whose bit is already set repeats an earlier pair's
-  // expert (bit j of `rep`) and is dropped.
-  constexpr int KB = 8;
-  unsigned long long rep = 0ull;
-  for (int j0 = 0; j0 < k; j0 += KB) {
-    int e[KB];
+  if (threadIdx.x < kPermChunk) {
+    // One lane per token sets the token's bits in pair order, so a pair whose bit is already set
+    // repeats an earlier pair's expert and is dropped. The pairs' expert indices are loaded KB at a
+    // time, so that a pair's loads do not wait on the previous pair's atomics.
+    const int lane = threadIdx.x & 63, tb = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * kPermChunk + threadIdx.x;
+    const bool live = t < T;
+    constexpr int KB = 8;
+    for (int j0 = 0; j0 < k; j0 += KB) {
+      int e[KB];
 #pragma unroll
-    for (int i = 0; i < KB; ++i) e[i] = (live && j0 + i < k) ? idx[t * k + j0 + i] : -1;
+      for (int i = 0; i < KB; ++i) e[i] = (live && j0 + i < k) ? idx[t * k + j0 + i] : -1;
 #pragma unroll
-    for (int i = 0; i < KB; ++i)
-      if (e[i] >= 0 && e[i] < E && (atomicOr(&bits[wave * E + e[i]], 1ull << lane) >> lane & 1ull))
-        rep |= 1ull << (j0 + i);
+      for (int i = 0; i < KB; ++i) {
+        if (j0 + i >= k) break;
+        int v = -1;
+        if (e[i] >= 0 && e[i] < E && !(atomicOr(&bits[tb * E + e[i]], 1ull << lane) >> lane & 1ull)) v = e[i];
+        pair_e[threadIdx.x * k + j0 + i] = v;
+      }
+    }
   }
   __syncthreads();
-  if (!live) return;
+  // four lanes per token rank and store its pairs (lane group g: pairs g, g + 4, ...)
+  const int ti = threadIdx.x % kPermChunk, g = threadIdx.x / kPermChunk;
+  const int lane = ti & 63, tb = ti >> 6;
+  const int64_t t = (int64_t)blockIdx.x * kPermChunk + ti;
+  if (t >= T) return;
   const unsigned long long below = (1ull << lane) - 1ull;
-  for (int j0 = 0; j0 < k; j0 += KB) {
-    int e[KB], base[KB];
-#pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      e[i] = j0 + i < k ? idx[t * k + j0 + i] : -1;
-      if (e[i] >= E || (rep >> ((j0 + i) & 63) & 1ull)) e[i] = -1;
+  for (int j = g; j < k; j += kPermLanes) {
+    const int e = pair_e[ti * k + j];
+    int32_t slot = -1;
+    if (e >= 0) {
+      int r = base_e[e];
+      for (int b = 0; b < tb; ++b) r += __popcll(bits[b * E + e]);
+      r += __popcll(bits[tb * E + e] & below);
+      slot = r;
+      sorted_token[r] = (int32_t)t;
     }
-#pragma unroll
-    for (int i = 0; i < KB; ++i) base[i] = e[i] >= 0 ? base_e[e[i]] : 0;
-#pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      if (j0 + i >= k) break;
-      int32_t slot = -1;
-      if (e[i] >= 0) {
-        int r = base[i];
-        for (int w = 0; w < wave; ++w) r += __popcll(bits[w * E + e[i]]);
-        r += __popcll(bits[wave * E + e[i]] & below);
-        slot = r;
-        sorted_token[r] = (int32_t)t;
-      }
-      slot_of_pair[t * k + j0 + i] = slot;
-    }
+    slot_of_pair[t * k + j] = slot;
   }
 }
 
@@ -212,8 +219,8 @@ hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* offs
                                  kMaxExpertsLds * 8 * (kPermChunk / 64));
     });
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(perm_count_kernel, dim3(chunks), dim3(kPermChunk), (size_t)E * 8 * (kPermChunk / 64), s, idx,
-                       T, E, k, cc);
+    hipLaunchKernelGGL(perm_count_kernel, dim3(chunks), dim3(kPermThreads), (size_t)E * 8 * (kPermChunk / 64), s,
+                       idx, T, E, k, cc);
   }
   {
     KernelTimer timer("perm_scan", s);
@@ -221,16 +228,18 @@ hipError_t launch_permute(const int32_t* idx, int T, int E, int k, int32_t* offs
   }
   {
     KernelTimer timer("perm_scatter", s);
-    // the masks and bases pass the default 64 KB of dynamic LDS at the largest expert counts
+    // the masks, bases and pair experts pass the default 64 KB of dynamic LDS at the largest expert
+    // counts and k
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
       attr = hipFuncSetAttribute((const void*)perm_scatter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 kMaxExpertsLds * (8 * (kPermChunk / 64) + 4));
+                                 kMaxExpertsLds * (8 * (kPermChunk / 64) + 4) + kPermChunk * kMaxTopKLds * 4);
     });
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(perm_scatter_kernel, dim3(chunks), dim3(kPermChunk), (size_t)E * (8 * (kPermChunk / 64) + 4), s,
-                       idx, T, E, k, cc, offsets, sorted_token, slot_of_pair);
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(chunks), dim3(kPermThreads),
+                       (size_t)E * (8 * (kPermChunk / 64) + 4) + (size_t)kPermChunk * k * 4, s, idx, T, E, k, cc,
+                       offsets, sorted_token, slot_of_pair);
   }
   return hipGetLastError();
 }
