@@ -95,9 +95,9 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ sco
   __shared__ int win_e[4][65];  // ranks 0..k, k <= 64
   __shared__ uint32_t win_key[4][65];
   __shared__ float win_s[4][65];
-  __shared__ int cand_e[4][64];
-  __shared__ uint32_t cand_key[4][64];
-  __shared__ float cand_s[4][64];
+  __shared__ int cand_e[4][65];  // candidates of the candidate pass (<= 64) or the k+1 winners of the exact pass
+  __shared__ uint32_t cand_key[4][65];
+  __shared__ float cand_s[4][65];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 4 + wv;
   if (t >= T) return;  // the whole wave leaves together
@@ -216,31 +216,36 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ sco
       if ((p && key[i] > kth) || (eq && eq_before + __popcll(m & lower_lanes) < need_eq)) sel |= 1u << i;
       eq_before += __popcll(m);
     }
-    int place[NPL];
+    // The kk winners go to LDS in lane order, then each is ranked against all of them (key, then
+    // index): one LDS pass instead of a rank counter per key in registers, which keeps the kernel's
+    // registers at the candidate pass's count (eight waves per SIMD).
+    int own_sel = __popc(sel);
+    int pos = 0;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) place[i] = 0;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      uint64_t m = __ballot((sel >> j) & 1u);
-      while (m) {
-        const int src = __builtin_ctzll(m);
-        m &= m - 1;
-        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key[j], src);
-        const int ej = src + 64 * j;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-          const int ei = lane + 64 * i;
-          place[i] += (kj > key[i] || (kj == key[i] && ej < ei)) ? 1 : 0;
-        }
-      }
-    }
+    for (int b = 0; b < CB; ++b) pos += __popcll(__ballot((own_sel >> b) & 1) & lower_lanes) << b;
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
       if ((sel >> i) & 1u) {
-        win_e[wv][place[i]] = lane + 64 * i;
-        win_key[wv][place[i]] = key[i];
-        win_s[wv][place[i]] = sv[i];
+        cand_key[wv][pos] = key[i];
+        cand_e[wv][pos] = lane + 64 * i;
+        cand_s[wv][pos] = sv[i];
+        ++pos;
       }
+    __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in issue order
+    for (int c = lane; c < kk; c += 64) {
+      const uint32_t ck = cand_key[wv][c];
+      const int ce = cand_e[wv][c];
+      const float cs = cand_s[wv][c];
+      int place = 0;
+      for (int j = 0; j < kk; ++j) {
+        const uint32_t kj = cand_key[wv][j];
+        const int ej = cand_e[wv][j];
+        place += (kj > ck || (kj == ck && ej < ce)) ? 1 : 0;
+      }
+      win_e[wv][place] = ce;
+      win_key[wv][place] = ck;
+      win_s[wv][place] = cs;
+    }
   }
   __builtin_amdgcn_wave_barrier();
   const int my_idx = lane < k ? win_e[wv][lane] : 0;
