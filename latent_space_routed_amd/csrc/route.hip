@@ -342,7 +342,7 @@ __global__ void __launch_bounds__(kHistThreads)
 // crosses c* walks its bins to j*, interpolates in f64 and moves the bias; then the row is zeroed.
 // ------------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) qb_update_kernel(uint32_t* __restrict__ hist, int E, int k, int nb,
-                                                        int64_t n_acc, float* __restrict__ bias) {
+                                                        int64_t n_acc, float* __restrict__ bias, bool al16) {
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (e >= E) return;
@@ -355,8 +355,22 @@ __global__ void __launch_bounds__(256) qb_update_kernel(uint32_t* __restrict__ h
   uint32_t hv[R];
   uint64_t lsum = 0;
   const bool cached = j1 - j0 <= R;
+  // whole 16-byte groups when every lane's run starts on 16 bytes (nb = 1000: 4 loads of 4 bins
+  // instead of 16 of one); a lane's run is then a whole number of groups
+  const bool vec = al16 && bpl <= R && bpl % 4 == 0 && nb % 4 == 0;
+  if (vec) {
 #pragma unroll
-  for (int i = 0; i < R; ++i) hv[i] = (cached && j0 + i < j1) ? h[j0 + i] : 0u;
+    for (int q = 0; q < R / 4; ++q) {
+      const uint4 v = j0 + 4 * q < j1 ? *reinterpret_cast<const uint4*>(h + j0 + 4 * q) : make_uint4(0, 0, 0, 0);
+      hv[4 * q] = v.x;
+      hv[4 * q + 1] = v.y;
+      hv[4 * q + 2] = v.z;
+      hv[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < R; ++i) hv[i] = (cached && j0 + i < j1) ? h[j0 + i] : 0u;
+  }
   if (cached) {
 #pragma unroll
     for (int i = 0; i < R; ++i) lsum += hv[i];
@@ -396,7 +410,13 @@ __global__ void __launch_bounds__(256) qb_update_kernel(uint32_t* __restrict__ h
       }
     }
   }
-  for (int j = j0; j < j1; ++j) h[j] = 0;
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < R / 4; ++q)
+      if (j0 + 4 * q < j1) *reinterpret_cast<uint4*>(h + j0 + 4 * q) = make_uint4(0, 0, 0, 0);
+  } else {
+    for (int j = j0; j < j1; ++j) h[j] = 0;
+  }
 }
 
 template <int NPL, bool PART>
@@ -479,7 +499,9 @@ hipError_t launch_qb_hist(const float* scores, const float* bias, const int32_t*
 
 hipError_t launch_qb_update(uint32_t* hist, int E, int k, int nb, int64_t n_acc, float* bias, hipStream_t s) {
   KernelTimer timer("qb_update", s);
-  hipLaunchKernelGGL(qb_update_kernel, dim3((unsigned)ceil_div(E, 4)), dim3(256), 0, s, hist, E, k, nb, n_acc, bias);
+  const bool al16 = reinterpret_cast<uintptr_t>(hist) % 16 == 0;
+  hipLaunchKernelGGL(qb_update_kernel, dim3((unsigned)ceil_div(E, 4)), dim3(256), 0, s, hist, E, k, nb, n_acc, bias,
+                     al16);
   return hipGetLastError();
 }
 
