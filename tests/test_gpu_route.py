@@ -78,11 +78,14 @@ def test_route_topk_ordering(name):
                                   O.qb_histogram(s, bias, ref_idx, ref_thr, cfg.n_bins))
 
 
+@pytest.mark.parametrize("offset", [0, 1])
 @pytest.mark.parametrize("nb", [2, 100, 1000, 1024, 1025, 4096, 32768])
-def test_qb_update_bin_counts(nb):
+def test_qb_update_bin_counts(nb, offset):
     """QB bias update on synthetic histograms whose rows each sum to N_acc (concentrated on a band of
     bins, one row all in one bin, one row spread evenly), bit-exact against the oracle for bin counts
-    that give one to 512 bins per lane (the kernel keeps up to 16 per lane in registers)."""
+    that give one to 512 bins per lane (the kernel keeps up to 16 per lane in registers). offset 1
+    passes a histogram that starts 4 bytes into its allocation (not 16-byte aligned), which takes the
+    kernel's one-bin accesses instead of its 16-byte ones."""
     E, k, n_acc = 37, 5, 5000
     rng = np.random.default_rng(nb)
     hist = np.zeros((E, nb), dtype=np.uint32)
@@ -101,9 +104,10 @@ def test_qb_update_bin_counts(nb):
     bias0 = (rng.standard_normal(E) * 0.01).astype(np.float32)
     cfg = replace(CONFIGS["mid_bf16"], T=64, d_model=128, n_experts=E, top_k=k, n_bins=nb)
     shape = C.make_shape(cfg, 64)
-    hd = torch.from_numpy(hist.view(np.int32).copy()).cuda()
+    flat = np.concatenate([np.zeros(offset, dtype=np.int32), hist.view(np.int32).ravel()])
+    hd = torch.from_numpy(flat).cuda()[offset:].view(E, nb)
     bd = torch.from_numpy(bias0.copy()).cuda()
-    say(f"qb_update E={E} k={k} nb={nb} n_acc={n_acc}")
+    say(f"qb_update E={E} k={k} nb={nb} n_acc={n_acc} offset={offset}")
     C.lmoe_qb_update(shape, hd, n_acc, bd)
     torch.cuda.synchronize()
     want, _ = O.qb_update(hist, n_acc, bias0, k)
