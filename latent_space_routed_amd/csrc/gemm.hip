@@ -138,6 +138,7 @@ __device__ inline void store_out(const GemmArgs& p, int64_t off, float v) {
 // ------------------------------------------------------------------------------------------------
 struct TileInfo {
   int g, n0, row0, rows;
+  int mtg = 1;    // m-tiles of the tile's group (grouped GEMMs)
   int k0, klen;   // contraction range of the tile (elements)
   int64_t coff;   // element offset of the tile's output block (K-grouped GEMMs)
 };
@@ -181,6 +182,7 @@ __device__ inline bool assign_tile(const GemmArgs& p, TileInfo& t, int vb) {
     t.g = lo;
     const int ms0 = p.mtile_start[lo];
     const int mtg = p.mtile_start[lo + 1] - ms0;
+    t.mtg = mtg;
     const int r = lt - n_tiles * ms0;
     n_tile = r / mtg;
     t.row0 = p.goff[lo] + (r % mtg) * BM;
@@ -235,6 +237,7 @@ __device__ inline bool assign_tile_after(const GemmArgs& p, TileInfo& t, int vb,
   t.coff = 0;
   const int ms0 = p.mtile_start[g];
   const int mtg = p.mtile_start[g + 1] - ms0;
+  t.mtg = mtg;
   const int r = lt - n_tiles * ms0;
   t.row0 = p.goff[g] + (r % mtg) * BM;
   t.rows = min(BM, p.goff[g + 1] - t.row0);
@@ -727,7 +730,14 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
         a_voff[i] = r * (int)a_ld + ch;
     }
   };
+  // B streams with the non-temporal hint when its group has one m-tile (read once); a group of
+  // several m-tiles reads the same weight slices once per m-tile, and those tiles run close together
+  // on one XCD, so there B is loaded plainly and the later m-tiles find it cached (measured on
+  // batches of 32768 tokens, about three m-tiles per expert: GEMM2 2.93 -> 2.75 ms, GEMM1 within
+  // 1 %; at 8192 tokens, one m-tile per expert, unchanged).
+  bool b_nt = true;
   auto set_b = [&](const TileInfo& tt) __attribute__((always_inline)) {
+    b_nt = tt.mtg == 1;
     const char* Bb = static_cast<const char*>(p.B) + (int64_t)tt.g * p.b_gstride * (int64_t)sizeof(TI);
     const int ncols = min(BNO, p.N - tt.n0);
     b_desc0 = make_desc(Bb + (int64_t)tt.n0 * b_ld, (int)(ncols * b_ld));
@@ -745,7 +755,10 @@ __global__ void __launch_bounds__(WAVES_M* WAVES_N* kWave)
 #pragma unroll
     for (int i = 0; i < B_PWI; ++i) {
       const bool up = GLU && (wi * B_PWI + i) * RPD >= BNO;
-      dma16_nt(up ? b_desc1 : b_desc0, b_voff[i], kt * KB, base + (wi * B_PWI + i) * 1024);
+      if (b_nt)
+        dma16_nt(up ? b_desc1 : b_desc0, b_voff[i], kt * KB, base + (wi * B_PWI + i) * 1024);
+      else
+        dma16(up ? b_desc1 : b_desc0, b_voff[i], kt * KB, base + (wi * B_PWI + i) * 1024);
     }
   };
   constexpr int KS = KB / 32;
