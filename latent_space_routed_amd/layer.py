@@ -46,10 +46,11 @@ class LatentMoE:
         # Fused path with shared experts: their GEMM1 depends on x alone, so it can run on a side
         # stream forked at the start of the step, beside the router, top-k, histogram,
         # down-projection and permutation, whose small kernels and the down-projection's last
-        # partial round of tiles leave CUs idle; the caller's stream waits for it before the
-        # up-projection. Outputs are bit-identical either way. Measured (one process, on and off
-        # alternating): K3 prefill 4.47-4.48 ms per step against 4.52, the routed experts' call
-        # unchanged; K3 decode 1.89 against 1.91; the tiny f32 workload 0.112-0.120 against 0.108,
+        # partial round of tiles leave CUs idle; the caller's stream waits for it before the routed
+        # GEMMs (joining later, before the up-projection, measured 0.01 ms slower at K3 prefill and
+        # 0.2 ms slower at 32768 tokens). Outputs are bit-identical either way. Measured (one
+        # process, on and off alternating): K3 prefill 4.47-4.48 ms per step against 4.52; K3
+        # decode 1.89 against 1.91; the tiny f32 workload 0.112-0.120 against 0.108,
         # where the fork and join cost more than the overlap gives; with MX routed experts at K3
         # prefill 3.61-3.66 against 3.60-3.61; K3 dimensions at 32768 tokens 16.79-16.87 against
         # 16.29-16.32, where the longer shared GEMM still runs when the routed GEMMs start. Forking
@@ -127,13 +128,11 @@ class LatentMoE:
                             ("ws_glu", C.LMOE_CALL_GROUPED_GLU), ("ws_combine", C.LMOE_CALL_COMBINE_NORM_UP)):
             n = C.workspace_bytes(shape, which)
             b[name] = torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
-        if self.fused and S > 0:
-            # the side stream's shared GEMM1 runs beside the router's and the down-projection's
-            # calls, which have workspaces of their own: it gets one too
-            # (allocated whether or not overlap_shared is set, so the flag can change between steps)
-            b["ws_glu_side"] = torch.empty_like(b["ws_glu"])
-            if self._side is None:
-                self._side = torch.cuda.Stream(device=dev)
+        if self.fused and S > 0 and self._side is None:
+            # created whether or not overlap_shared is set, so the flag can change between steps; the
+            # side stream's shared GEMM1 uses the grouped-GLU workspace, which the routed GEMMs use
+            # only after the join
+            self._side = torch.cuda.Stream(device=dev)
         self._bufs = b
 
     def _overlapped(self, T: int) -> bool:
@@ -172,7 +171,7 @@ class LatentMoE:
             side.wait_stream(cur)
             with torch.cuda.stream(side):
                 C.lmoe_grouped_situ_glu(shape, 1, T, D, S * Is, D, x, None, self.w1s_packed, None, b["h_s"], None,
-                                        b["ws_glu_side"])
+                                        b["ws_glu"])
         C.lmoe_route(shape, x, w["w_router"], self.bias, w.get("logit_offset"), b["scores"], b["idx"], b["w"],
                      b["thresh"], b["ws_route"], w_router_split=self.w_router_split)
         if accumulate_hist:
@@ -181,6 +180,8 @@ class LatentMoE:
         fused = self.fused
         C.lmoe_permute(shape, x, w["w_down"], b["idx"], b["x_lat"], b["offsets"], b["sorted_token"],
                        b["slot_of_pair"], None if fused else b["x_perm"], b["ws_permute"])
+        if side is not None:
+            cur.wait_stream(side)  # h_s is ready, and the routed GEMMs have the chip to themselves
         if self.mx:
             C.lmoe_mx_quantize(shape, C.LMOE_MX_FP8, T, L, b["x_lat"], b["x_lat_codes"], b["x_lat_scales"])
             (w1c, w1s), (w2c, w2s) = self.mx_w["w1"], self.mx_w["w2"]
@@ -193,14 +194,10 @@ class LatentMoE:
         else:
             C.lmoe_grouped_situ_glu(shape, E, T * k, L, I, L, b["x_perm"], b["offsets"], w["w1"], w["w2"], b["h"],
                                     b["y"], b["ws_glu"])
-        if side is not None:
-            C.lmoe_combine_norm(shape, b["y"], b["slot_of_pair"], b["w"], w.get("gamma"), b["n"])
-            cur.wait_stream(side)  # h_s is ready
-            C.lmoe_up_project(shape, b["n"], w["w_up"], None, b["out"], h_shared=b["h_s"], w2_shared=self.w2s_packed,
-                              workspace=b["ws_combine"])
-        elif S > 0 and fused:
-            C.lmoe_grouped_situ_glu(shape, 1, T, D, S * Is, D, x, None, self.w1s_packed, None, b["h_s"], None,
-                                    b["ws_glu"])
+        if S > 0 and fused:
+            if side is None:
+                C.lmoe_grouped_situ_glu(shape, 1, T, D, S * Is, D, x, None, self.w1s_packed, None, b["h_s"], None,
+                                        b["ws_glu"])
             C.lmoe_combine_norm_up(shape, b["y"], b["slot_of_pair"], b["w"], w.get("gamma"), w["w_up"], None,
                                    b["n"], b["out"], h_shared=b["h_s"], w2_shared=self.w2s_packed,
                                    workspace=b["ws_combine"])

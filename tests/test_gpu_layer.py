@@ -201,10 +201,10 @@ def test_deterministic(run):
 
 
 def test_side_stream_and_split_calls_bit_identical(run):
-    """With the side stream on, the fused layer runs the shared GEMM1 on a stream forked
-    at the start of the step, beside the routing, down-projection, permutation and routed experts,
-    then joins for lmoe_up_project after lmoe_combine_norm; off, it calls lmoe_combine_norm_up on one
-    stream. Both give the same n, h_s and out bit for bit (same kernels, same per-stream order)."""
+    """With the side stream on, the fused layer runs the shared GEMM1 on a stream forked at the start
+    of the step, beside the routing, down-projection and permutation, and joins before the routed
+    experts; off, every call runs on one stream. Both give the same n, h_s and out bit for bit (same
+    kernels, same per-stream order)."""
     cfg, inp, layer, x, g, ref = run
     if not g["fused"] or cfg.n_shared == 0:
         pytest.skip("the side stream is used on the fused path with shared experts")
