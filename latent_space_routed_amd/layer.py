@@ -52,11 +52,11 @@ class LatentMoE:
         # process, on and off alternating): K3 prefill 4.47-4.48 ms per step against 4.52; K3
         # decode 1.89 against 1.91; the tiny f32 workload 0.112-0.120 against 0.108,
         # where the fork and join cost more than the overlap gives; with MX routed experts at K3
-        # prefill 3.61-3.66 against 3.60-3.61; K3 dimensions at 32768 tokens 16.79-16.87 against
+        # prefill 3.64-3.65 against 3.66-3.67; K3 dimensions at 32768 tokens 16.79-16.87 against
         # 16.29-16.32, where the longer shared GEMM still runs when the routed GEMMs start. Forking
         # after the route or after the permutation instead makes the routed GEMMs share the chip
-        # (slower). None (the default) turns it on for bf16/f32 routed experts when the shared
-        # GEMM1 of the batch is at least 1 GFLOP and the batch holds at most 16384 tokens.
+        # (slower). None (the default) turns it on when the shared GEMM1 of the batch is at least
+        # 1 GFLOP and the batch holds at most 16384 tokens.
         self.overlap_shared = overlap_shared
         self._side = None
         if mx and (cfg.act_dtype != "bf16" or not fused):
@@ -138,8 +138,6 @@ class LatentMoE:
     def _overlapped(self, T: int) -> bool:
         cfg = self.cfg
         if not (self.fused and cfg.n_shared > 0) or self.overlap_shared is False:
-            return False
-        if self.overlap_shared is None and self.mx:
             return False
         if self.overlap_shared:
             return True

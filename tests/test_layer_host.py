@@ -33,7 +33,6 @@ def test_side_stream_explicit_setting_and_exclusions():
     cfg = CONFIGS["k3_prefill"]
     assert overlapped(cfg, overlap=True) and not overlapped(cfg, overlap=False)
     assert overlapped(CONFIGS["tiny_f32"], overlap=True)  # forced on below the threshold
-    assert not overlapped(cfg, mx=True)                   # MX routed experts: off unless asked for
-    assert overlapped(cfg, mx=True, overlap=True)
+    assert overlapped(cfg, mx=True) and not overlapped(cfg, mx=True, overlap=False)
     assert not overlapped(cfg, fused=False, overlap=True)  # the unfused path adds f32 y_sh on one stream
     assert not overlapped(replace(cfg, n_shared=0), overlap=True)
