@@ -553,7 +553,8 @@ def main() -> int:
         "ms_per_step_min": head["ms_min"],
         "ms_per_step_mean": head["ms_mean"],
         "timing": "median of per-step HIP events; a 512 MB write flushes the MALL before each step, outside "
-                  "the events; two batches alternate; the bias update runs every step",
+                  "the events; two batches alternate; the bias update runs every step; the shared experts' "
+                  "GEMM1 runs on a second stream up to the routed experts unless --one-stream",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -564,7 +565,8 @@ def main() -> int:
                    "inter_shared": cfg.inter_shared, "n_bins": cfg.n_bins, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "kernels_ms_per_step": head["kernels_ms_per_step"],
-        "kernels_note": "a pass of its own after the timed region, HIP events around every kernel",
+        "kernels_note": "a pass of its own after the timed region, every kernel on one stream, HIP events around "
+                        "every kernel",
         "kernels_roofline": head["kernels_roofline"],
     }
     if "qb" in head:
