@@ -155,14 +155,16 @@ def test_topk_candidate_pass_boundary():
     np.testing.assert_allclose(wts.cpu().numpy(), ref_w, rtol=3e-7, atol=0)
 
 
-@pytest.mark.parametrize("E", [2048, 1001])
-def test_permute_large_expert_counts(E):
+@pytest.mark.parametrize("E,k", [(2048, 16), (1001, 16), (2048, 64), (1001, 7)])
+def test_permute_large_expert_counts(E, k):
     """The permutation at expert counts whose per-chunk masks and bases need more than the default
-    64 KB of LDS (E = 2048, the largest the library takes) and at an odd count, on random routing
-    with some experts left empty: offsets, sorted tokens and slots bit-exact against the oracle."""
-    T, D, k = 700, 128, 16
+    64 KB of LDS (E = 2048, the largest the library takes; with k = 64, the largest k, the scatter's
+    LDS also holds 64 KB of pair experts) and at an odd count and an odd k (a token's pairs spread
+    unevenly over its four lanes), on random routing with some experts left empty: offsets, sorted
+    tokens and slots bit-exact against the oracle."""
+    T, D = 700, 128
     cfg = replace(CONFIGS["mid_bf16"], T=T, d_model=D, n_experts=E, top_k=k)
-    rng = np.random.default_rng(E)
+    rng = np.random.default_rng(E + k)
     # each token picks k distinct experts from the first 3/4 of the experts: the rest stay empty
     idx = np.stack([rng.choice(3 * E // 4, k, replace=False) for _ in range(T)]).astype(np.int32)
     dev = "cuda"
