@@ -29,7 +29,10 @@ MID = CONFIGS["mid_bf16"]
 # (config, gain_bias): gain_bias draws gamma = 1 + 0.5 N(0,1) and b = 0.05 N(0,1)
 SMALL_CASES = [(TINY, False), (replace(TINY, name="tiny_gb"), True), (replace(TINY, name="tiny_ragged_gb", T=77), True),
                (replace(TINY, name="tiny_big_gb", T=1024), True), (MID, False),
-               (replace(MID, name="mid_ragged_gb", T=1000), True)]
+               (replace(MID, name="mid_ragged_gb", T=1000), True),
+               # narrow bf16 experts with few rows each: the routed GEMMs on 128-row tiles (the
+               # register pipeline), which wider bf16 experts no longer take
+               (replace(MID, name="mid_narrow_gb", T=300, d_latent=512, inter=128), True)]
 # fused: routed GEMM gathers x_lat rows, shared down-projection folded into the up-projection;
 # unfused: x_perm and y_sh materialised
 RUNS = [(c, gb, f) for c, gb in SMALL_CASES for f in (True, False)]
